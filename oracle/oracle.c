@@ -1,0 +1,509 @@
+/*
+ * CPU oracle for the forward pass of one Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code with
+ * the HIP path: no header, helper, table or constant generator is common to
+ * the two. Both sides take their inputs from the seeded generators, which hold
+ * none of the layer's arithmetic.
+ *
+ * What the layer computes, and where the pages state it:
+ *   - router in fp32, whatever the activation dtype
+ *       (moe-200m-qwen3-100b README, "Per-layer numerics", first item;
+ *        "SigmoidRouter": logits = x W_r^T on fp32 copies of both operands);
+ *   - sigmoid scores, selection on scores plus a per-expert bias that moves
+ *     selection only; combine weights gathered from the unbiased scores and
+ *     divided by their sum plus 1e-9
+ *       ("SigmoidRouter"; SpecForge PR #930, "What this adds" and "Tests");
+ *   - softmax over all experts, top-k weights renormalised, no scaling, no
+ *     shared expert (SpecForge PR #930, "What this adds", the qwen3 preset);
+ *   - top-k sorted by descending selection value ("SigmoidRouter": topk);
+ *   - tokens per expert ("SigmoidRouter": one-hot sum over tokens);
+ *   - SwiGLU experts with weights stacked [E, out, in], an optional shared
+ *     expert that every token uses with weight 1, and a weighted sum of the
+ *     expert outputs (README "Architecture diagram"; PR #930 "Why FSDP is
+ *     enough here").
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes of the repository):
+ *   - the fp32 gate product is one fused-multiply-add chain per (token,
+ *     expert), over features in ascending order, starting from +0;
+ *   - with no bias the selection value is the logit itself (softmax and
+ *     sigmoid are strictly increasing, so the chosen set and order are those
+ *     of the scores, with no rounding of exp in the way);
+ *   - the bias is added to the score (sigmoid, or softmax probability);
+ *   - exp inside the router is the canonical fp32 function cexpf below;
+ *   - ties are broken towards the lower expert index;
+ *   - softmax weights are exp(l_j - M) / sum_i exp(l_i - M) over the k
+ *     selected logits, M their maximum (equal to p_j / sum p_i in real
+ *     arithmetic because the full normaliser cancels);
+ *   - sums over slots and over experts run in ascending index order;
+ *   - rows of one expert are ordered by ascending token index;
+ *   - the expert MLPs and the combine run in fp64 on the exact values of the
+ *     inputs (bf16 widens exactly), so the oracle's own rounding is far below
+ *     any tolerance used against it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define DT_F32 0
+#define DT_BF16 1
+#define SCORE_SOFTMAX 0
+#define SCORE_SIGMOID 1
+
+/* ------------------------------------------------------------------------ */
+/* element access                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Element i of a row-major array holding fp32 values or bf16 bit patterns. */
+static float elem(const void *p, int dtype, size_t i)
+{
+    if (dtype == DT_BF16)
+        return bf16_to_float(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+static float bits_to_float(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* canonical fp32 exp                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * exp(a) in fp32 from IEEE +, -, *, / and fma only, so that any machine with
+ * IEEE arithmetic gets the same bits.
+ *   1. n = nearest integer to a / ln 2 (a * log2(e), rounded half to even).
+ *   2. r = a - n ln 2 with ln 2 split into two fp32 constants (Cody and
+ *      Waite, 1980): hi = ln 2 rounded to fp32, lo = (ln 2 - hi) rounded to
+ *      fp32; each step is one fma. |r| <= about 0.347.
+ *   3. exp(r) by its Taylor series to degree 7 in Horner form with fma; the
+ *      dropped term is below r^8/8! < 6e-9 relative, under half an fp32 ulp.
+ *   4. exp(a) = exp(r) * 2^n, the power of two built from its bit pattern;
+ *      when 2^n itself is not a normal fp32 the scaling is split in two so
+ *      that only the final multiply rounds (subnormal results included).
+ * Overflow above 88.72283935546875 gives +inf, underflow below
+ * -103.972084045410 gives +0 (exp there is under half the least subnormal).
+ */
+float oracle_cexpf(float a)
+{
+    const float LOG2E = 1.44269504088896340736f;
+    const float LN2_HI = 0.693147182464599609375f;      /* fp32(ln 2) */
+    const float LN2_LO = -1.9046542121259336e-09f;     /* fp32(ln 2 - LN2_HI) */
+    const float C2 = 1.0f / 2.0f, C3 = 1.0f / 6.0f, C4 = 1.0f / 24.0f;
+    const float C5 = 1.0f / 120.0f, C6 = 1.0f / 720.0f, C7 = 1.0f / 5040.0f;
+    float n, r, p;
+    int ni;
+
+    if (a != a)
+        return a;
+    if (a > 88.72283935546875f)
+        return INFINITY;
+    if (a < -103.972084045410f)
+        return 0.0f;
+
+    n = rintf(a * LOG2E);
+    r = fmaf(-n, LN2_HI, a);
+    r = fmaf(-n, LN2_LO, r);
+
+    p = C7;
+    p = fmaf(p, r, C6);
+    p = fmaf(p, r, C5);
+    p = fmaf(p, r, C4);
+    p = fmaf(p, r, C3);
+    p = fmaf(p, r, C2);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+
+    ni = (int)n;
+    if (ni > 127)
+        return (p * 2.0f) * bits_to_float((uint32_t)(ni - 1 + 127) << 23);
+    if (ni < -126)
+        return (p * bits_to_float((uint32_t)(ni + 64 + 127) << 23)) * bits_to_float((uint32_t)(-64 + 127) << 23);
+    return p * bits_to_float((uint32_t)(ni + 127) << 23);
+}
+
+void oracle_cexpf_array(const float *a, float *out, int64_t n)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; i++)
+        out[i] = oracle_cexpf(a[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* router                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * logits[t, e] = sum_j x[t, j] * W_r[e, j] in fp32, as one fma chain over j
+ * ascending from +0 ("SigmoidRouter": F.linear on fp32 copies).
+ * Written with experts innermost so that the chains of one token run side by
+ * side; each chain still sees its terms in ascending j.
+ */
+void oracle_logits(int dtype, const void *x, int64_t T, int d, const float *w_router, int E, float *logits)
+{
+    float *wt = (float *)malloc(sizeof(float) * (size_t)d * (size_t)E); /* W_r transposed: [d][E] */
+    int64_t t;
+    int j, e;
+    for (e = 0; e < E; e++)
+        for (j = 0; j < d; j++)
+            wt[(size_t)j * E + e] = w_router[(size_t)e * d + j];
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; t++) {
+        float *acc = logits + (size_t)t * E;
+        int jj, ee;
+        for (ee = 0; ee < E; ee++)
+            acc[ee] = 0.0f;
+        for (jj = 0; jj < d; jj++) {
+            const float xv = elem(x, dtype, (size_t)t * d + jj);
+            const float *wrow = wt + (size_t)jj * E;
+            for (ee = 0; ee < E; ee++)
+                acc[ee] = fmaf(xv, wrow[ee], acc[ee]);
+        }
+    }
+    free(wt);
+}
+
+static float sigmoidf_canon(float l)
+{
+    return 1.0f / (1.0f + oracle_cexpf(-l));
+}
+
+/*
+ * Routing of one token from its fp32 logits l[0..E-1]: selection values,
+ * top-k, combine weights.
+ */
+static void route_token(const float *l, const float *bias, int E, int k, int score, int renorm,
+                        float *v, unsigned char *taken, int32_t *idx, float *w)
+{
+    int e, j;
+    float m = 0.0f, z = 0.0f;
+
+    /* Softmax normaliser over all experts: only needed for a softmax score
+     * that is biased or not renormalised. */
+    if (score == SCORE_SOFTMAX && (bias || !renorm)) {
+        m = l[0];
+        for (e = 1; e < E; e++)
+            if (l[e] > m)
+                m = l[e];
+        z = 0.0f;
+        for (e = 0; e < E; e++)
+            z += oracle_cexpf(l[e] - m);
+    }
+
+    /* selection value */
+    for (e = 0; e < E; e++) {
+        if (!bias)
+            v[e] = l[e];
+        else if (score == SCORE_SIGMOID)
+            v[e] = sigmoidf_canon(l[e]) + bias[e];
+        else
+            v[e] = oracle_cexpf(l[e] - m) / z + bias[e];
+    }
+
+    /* top-k: k times, the largest remaining value; on a tie the lower index
+     * is kept because only a strictly larger value replaces the candidate. */
+    memset(taken, 0, (size_t)E);
+    for (j = 0; j < k; j++) {
+        int best = -1;
+        for (e = 0; e < E; e++) {
+            if (taken[e])
+                continue;
+            if (best < 0 || v[e] > v[best])
+                best = e;
+        }
+        taken[best] = 1;
+        idx[j] = best;
+    }
+
+    /* combine weights from the unbiased scores */
+    if (score == SCORE_SOFTMAX) {
+        if (renorm) {
+            float mk = l[idx[0]], s = 0.0f;
+            for (j = 1; j < k; j++)
+                if (l[idx[j]] > mk)
+                    mk = l[idx[j]];
+            for (j = 0; j < k; j++) {
+                w[j] = oracle_cexpf(l[idx[j]] - mk);
+                s += w[j];
+            }
+            for (j = 0; j < k; j++)
+                w[j] = w[j] / s;
+        } else {
+            for (j = 0; j < k; j++)
+                w[j] = oracle_cexpf(l[idx[j]] - m) / z;
+        }
+    } else {
+        float s = 0.0f;
+        for (j = 0; j < k; j++) {
+            w[j] = sigmoidf_canon(l[idx[j]]);
+            s += w[j];
+        }
+        if (renorm)
+            for (j = 0; j < k; j++)
+                w[j] = w[j] / (s + 1e-9f);
+    }
+}
+
+/*
+ * Router for T tokens: idx [T, k] (slots in descending selection value),
+ * w [T, k] fp32, counts [E] (tokens per expert). logits_out [T, E] is
+ * optional. Returns 0, or -1 on bad arguments.
+ */
+int oracle_route(int dtype, const void *x, int64_t T, int d, const float *w_router, const float *sel_bias,
+                 int E, int k, int score, int renorm, int32_t *idx, float *w, int32_t *counts, float *logits_out)
+{
+    float *logits;
+    int64_t t;
+    int e;
+    if (T < 0 || d < 1 || E < 1 || k < 1 || k > E)
+        return -1;
+    logits = logits_out ? logits_out : (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+    oracle_logits(dtype, x, T, d, w_router, E, logits);
+#pragma omp parallel
+    {
+        float *v = (float *)malloc(sizeof(float) * (size_t)E);
+        unsigned char *taken = (unsigned char *)malloc((size_t)E);
+#pragma omp for schedule(static)
+        for (t = 0; t < T; t++)
+            route_token(logits + (size_t)t * E, sel_bias, E, k, score, renorm, v, taken, idx + (size_t)t * k,
+                        w + (size_t)t * k);
+        free(v);
+        free(taken);
+    }
+    for (e = 0; e < E; e++)
+        counts[e] = 0;
+    for (t = 0; t < T * k; t++)
+        counts[idx[t]]++;
+    if (!logits_out)
+        free(logits);
+    return 0;
+}
+
+/*
+ * Expert-contiguous order. offsets = exclusive scan of counts (E+1 entries);
+ * row_of[t, j] = offsets[e] + number of tokens t' < t that chose e, with
+ * e = idx[t, j]. Each token holds k distinct experts, so this is a stable
+ * ordering of the (token, slot) pairs by expert.
+ */
+int oracle_dispatch(int64_t T, int E, int k, const int32_t *idx, int32_t *counts, int32_t *offsets, int32_t *row_of)
+{
+    int32_t *cursor = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int64_t t;
+    int e, j;
+    for (e = 0; e < E; e++)
+        counts[e] = 0;
+    for (t = 0; t < T * k; t++) {
+        if (idx[t] < 0 || idx[t] >= E) {
+            free(cursor);
+            return -1;
+        }
+        counts[idx[t]]++;
+    }
+    offsets[0] = 0;
+    for (e = 0; e < E; e++)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (t = 0; t < T; t++)
+        for (j = 0; j < k; j++) {
+            e = idx[t * k + j];
+            row_of[t * k + j] = offsets[e] + cursor[e]++;
+        }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* experts                                                                   */
+/* ------------------------------------------------------------------------ */
+
+static double silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+#define PAIR_BLOCK 16
+
+/*
+ * SwiGLU expert outputs for a list of (row, expert) pairs, in fp64:
+ *   out[p] = W_down[e] (silu(W_gate[e] a) * (W_up[e] a)),  a = x[row[p]],
+ * with W_gate, W_up [E, d_ff, d] and W_down [E, d, d_ff]. The pairs are
+ * visited expert by expert (the "sorted loop"), PAIR_BLOCK rows at a time so
+ * that each weight row is read once per block.
+ */
+int oracle_experts(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, const int64_t *pair_row,
+                   const int32_t *pair_expert, int E, const void *w_gate, const void *w_up, const void *w_down,
+                   double *out)
+{
+    int64_t *order, *starts, n_blocks = 0, p;
+    int64_t *count;
+    int e;
+    if (n_pairs <= 0)
+        return 0;
+    /* stable counting sort of the pairs by expert */
+    count = (int64_t *)calloc((size_t)E + 1, sizeof(int64_t));
+    order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_pairs);
+    for (p = 0; p < n_pairs; p++) {
+        if (pair_expert[p] < 0 || pair_expert[p] >= E) {
+            free(count);
+            free(order);
+            return -1;
+        }
+        count[pair_expert[p] + 1]++;
+    }
+    for (e = 0; e < E; e++)
+        count[e + 1] += count[e];
+    {
+        int64_t *cur = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+        memcpy(cur, count, sizeof(int64_t) * (size_t)E);
+        for (p = 0; p < n_pairs; p++)
+            order[cur[pair_expert[p]]++] = p;
+        free(cur);
+    }
+    /* work items: blocks of up to PAIR_BLOCK pairs of one expert */
+    starts = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_pairs + E + 1));
+    for (e = 0; e < E; e++)
+        for (p = count[e]; p < count[e + 1]; p += PAIR_BLOCK)
+            starts[n_blocks++] = p;
+
+#pragma omp parallel
+    {
+        double *xb = (double *)malloc(sizeof(double) * (size_t)d * PAIR_BLOCK);   /* [d][B] */
+        double *hb = (double *)malloc(sizeof(double) * (size_t)d_ff * PAIR_BLOCK); /* [d_ff][B] */
+        double *wr = (double *)malloc(sizeof(double) * (size_t)(d > d_ff ? d : d_ff));
+        double *wr2 = (double *)malloc(sizeof(double) * (size_t)d);
+        int64_t bi;
+#pragma omp for schedule(dynamic, 1)
+        for (bi = 0; bi < n_blocks; bi++) {
+            int64_t s = starts[bi];
+            int ex = pair_expert[order[s]];
+            int64_t end = count[ex + 1];
+            int nb = (int)((end - s) < PAIR_BLOCK ? (end - s) : PAIR_BLOCK);
+            int b, i, f, c;
+            const size_t wg_off = (size_t)ex * d_ff * d, wd_off = (size_t)ex * d * d_ff;
+            for (b = 0; b < nb; b++) {
+                int64_t row = pair_row[order[s + b]];
+                for (i = 0; i < d; i++)
+                    xb[(size_t)i * PAIR_BLOCK + b] = (double)elem(x, dtype, (size_t)row * d + i);
+            }
+            /* gate and up projections, SwiGLU */
+            for (f = 0; f < d_ff; f++) {
+                double g[PAIR_BLOCK], u[PAIR_BLOCK];
+                for (b = 0; b < PAIR_BLOCK; b++)
+                    g[b] = u[b] = 0.0;
+                for (i = 0; i < d; i++) {
+                    wr[i] = (double)elem(w_gate, dtype, wg_off + (size_t)f * d + i);
+                    wr2[i] = (double)elem(w_up, dtype, wg_off + (size_t)f * d + i);
+                }
+                for (i = 0; i < d; i++) {
+                    const double *xi = xb + (size_t)i * PAIR_BLOCK;
+                    for (b = 0; b < PAIR_BLOCK; b++) {
+                        g[b] += wr[i] * xi[b];
+                        u[b] += wr2[i] * xi[b];
+                    }
+                }
+                for (b = 0; b < PAIR_BLOCK; b++)
+                    hb[(size_t)f * PAIR_BLOCK + b] = silu(g[b]) * u[b];
+            }
+            /* down projection */
+            for (c = 0; c < d; c++) {
+                double o[PAIR_BLOCK];
+                for (b = 0; b < PAIR_BLOCK; b++)
+                    o[b] = 0.0;
+                for (f = 0; f < d_ff; f++)
+                    wr[f] = (double)elem(w_down, dtype, wd_off + (size_t)c * d_ff + f);
+                for (f = 0; f < d_ff; f++) {
+                    const double *hf = hb + (size_t)f * PAIR_BLOCK;
+                    for (b = 0; b < PAIR_BLOCK; b++)
+                        o[b] += wr[f] * hf[b];
+                }
+                for (b = 0; b < nb; b++)
+                    out[(size_t)order[s + b] * d + c] = o[b];
+            }
+        }
+        free(xb);
+        free(hb);
+        free(wr);
+        free(wr2);
+    }
+    free(starts);
+    free(order);
+    free(count);
+    return 0;
+}
+
+/*
+ * The layer's output for a subset of tokens, in fp64:
+ *   y[t] = sum_{j<k} w[t, j] * E_{idx[t, j]}(x_t)  (+ S(x_t), weight 1)
+ * summed over slots in order, the shared expert added last
+ * (README "Architecture diagram": routed experts and the always-on shared
+ * expert feed one weighted sum). tokens [n_tok] lists the token ids; y is
+ * [n_tok, d]. The shared weights may be NULL.
+ */
+int oracle_combine(int dtype, int d, int d_ff, int d_ff_shared, const void *x, int64_t n_tok, const int64_t *tokens,
+                   int k, const int32_t *idx, const float *w, int E, const void *w_gate, const void *w_up,
+                   const void *w_down, const void *ws_gate, const void *ws_up, const void *ws_down, double *y)
+{
+    int64_t n_pairs = n_tok * k, p, i;
+    int64_t *prow = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+    int32_t *pexp = (int32_t *)calloc((size_t)(n_pairs > 0 ? n_pairs : 1), sizeof(int32_t));
+    double *o = (double *)malloc(sizeof(double) * (size_t)(n_pairs > 0 ? n_pairs : 1) * (size_t)d);
+    double *s = NULL;
+    int rc, j, c;
+    for (i = 0; i < n_tok; i++)
+        for (j = 0; j < k; j++) {
+            prow[i * k + j] = tokens[i];
+            pexp[i * k + j] = idx[tokens[i] * k + j];
+        }
+    rc = oracle_experts(dtype, d, d_ff, x, n_pairs, prow, pexp, E, w_gate, w_up, w_down, o);
+    if (rc == 0 && ws_gate) {
+        int32_t *zero = (int32_t *)calloc((size_t)(n_tok > 0 ? n_tok : 1), sizeof(int32_t));
+        s = (double *)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1) * (size_t)d);
+        rc = oracle_experts(dtype, d, d_ff_shared, x, n_tok, tokens, zero, 1, ws_gate, ws_up, ws_down, s);
+        free(zero);
+    }
+    if (rc == 0) {
+        for (i = 0; i < n_tok; i++)
+            for (c = 0; c < d; c++) {
+                double acc = 0.0;
+                for (j = 0; j < k; j++) {
+                    p = i * k + j;
+                    acc += (double)w[tokens[i] * k + j] * o[(size_t)p * d + c];
+                }
+                if (s)
+                    acc += s[(size_t)i * d + c];
+                y[(size_t)i * d + c] = acc;
+            }
+    }
+    free(prow);
+    free(pexp);
+    free(o);
+    free(s);
+    return rc;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

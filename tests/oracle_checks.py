@@ -1,0 +1,306 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each check takes the loaded oracle library (the real one, or a copy built with a
+planted mistake) and raises AssertionError when the oracle disagrees with
+* the mathematics (closed forms, error bounds, brute-force enumeration),
+* a library routine on a special case (numpy fp64 matmul, exp, stable argsort),
+* a property the pages state for the layer (weights renormalise to one and
+  match a per-token dense reference; the selection bias moves selection only:
+  SpecForge PR #930, "Tests"; the router in fp32: moe-200m-qwen3-100b README,
+  "Per-layer numerics"; SigmoidRouter's weight gather and renormalisation).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+import oracle
+from mixture_experts_ffn_02_amd.inputs import LayerConfig, bf16_bits_to_f32, f32_to_bf16_bits, make_layer
+
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+# ---------------------------------------------------------------------------
+# helpers (numpy fp64 references)
+# ---------------------------------------------------------------------------
+
+def widen(a: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def swiglu64(x64: np.ndarray, wg, wu, wd) -> np.ndarray:
+    """Textbook SwiGLU FFN in fp64 (Shazeer 2020): W_down (silu(W_gate x) * W_up x)."""
+    g = x64 @ widen(wg).T
+    u = x64 @ widen(wu).T
+    h = g / (1.0 + np.exp(-g)) * u
+    return h @ widen(wd).T
+
+
+def ulp32(v: np.ndarray) -> np.ndarray:
+    v = np.abs(v.astype(np.float32))
+    return np.spacing(v).astype(np.float64)
+
+
+def small_layer(T=96, d=64, E=8, k=2, d_ff=96, dtype="bf16", score="softmax", shared=False,
+                bias_range=0.0, seed=3):
+    cfg = LayerConfig("pin", T=T, d_model=d, n_experts=E, top_k=k, d_ff=d_ff, dtype=dtype, score=score,
+                      shared=shared, bias_range=bias_range, seed=seed)
+    return cfg, make_layer(cfg)
+
+
+# ---------------------------------------------------------------------------
+# canonical exp
+# ---------------------------------------------------------------------------
+
+def check_cexpf(L, stride: int = 61) -> None:
+    """cexpf within 2 ulp of fp64 exp over a dense sweep of fp32 inputs in
+    [-104, 89], plus its special values."""
+    lo = np.float32(-104.0).view(np.uint32)
+    hi = np.float32(89.0).view(np.uint32)
+    neg = np.arange(np.uint32(0x80000000), lo, stride, dtype=np.uint32).view(np.float32)
+    pos = np.arange(np.uint32(0), hi, stride, dtype=np.uint32).view(np.float32)
+    a = np.concatenate([neg, pos, np.float32([0.0, -0.0, 1.0, -1.0, 88.72283, -103.97207, -87.33655, 0.5,
+                                              -0.34657359, 0.34657359])])
+    got = oracle.cexpf(a, L=L).astype(np.float64)
+    ref = np.exp(a.astype(np.float64))
+    finite = np.isfinite(got) & (ref < float(np.finfo(np.float32).max))
+    err = np.abs(got[finite] - ref[finite]) / ulp32(ref[finite])
+    assert err.max() <= 2.0, f"cexpf error {err.max():.3f} ulp at {a[finite][err.argmax()]!r}"
+    spec = oracle.cexpf(np.float32([0.0, 89.0, -105.0, 88.72283935546875, -103.97207641601562]), L=L)
+    assert spec[0] == 1.0 and np.isposinf(spec[1]) and spec[2] == 0.0 and np.isposinf(spec[3])
+    assert spec[4] == np.float32(2.0 ** -149)
+
+
+# ---------------------------------------------------------------------------
+# logits
+# ---------------------------------------------------------------------------
+
+def check_logits(L) -> None:
+    """fp32 fma-chain logits: within the Higham bound gamma_d * sum|x||w| of the
+    fp64 dot product; exact where every partial sum is exact; and summed in
+    ascending feature order (a case where the order decides the result)."""
+    cfg, inp = small_layer(T=128, d=320, E=16)
+    x, wr = inp["x"], inp["w_router"]
+    lg = oracle.logits(x, wr, L=L).astype(np.float64)
+    x64 = widen(x)
+    ref = x64 @ wr.astype(np.float64).T
+    d = x.shape[1]
+    gamma = d * U32 / (1 - d * U32)
+    bound = gamma * (np.abs(x64) @ np.abs(wr.astype(np.float64)).T)
+    assert np.all(np.abs(lg - ref) <= bound + 1e-30), "logits outside the fp32 summation error bound"
+    # small integers: every product and partial sum is exact in fp32
+    rng = np.random.default_rng(7)
+    xi = rng.integers(-8, 9, size=(40, 96)).astype(np.float32)
+    wi = rng.integers(-8, 9, size=(12, 96)).astype(np.float32)
+    assert np.array_equal(oracle.logits(xi, wi, L=L), (xi.astype(np.int64) @ wi.astype(np.int64).T).astype(np.float32))
+    # order: 2^24 + 1 - 2^24 is 0 in an ascending fp32 chain (the +1 is lost),
+    # while any chain that adds the two large terms first gives 1.
+    xo = np.float32([[2.0 ** 24, 1.0, -(2.0 ** 24), 0.0]])
+    wo = np.float32([[1.0, 1.0, 1.0, 1.0], [0.0, 1.0, 0.0, 0.0]])
+    got = oracle.logits(xo, wo, L=L)
+    assert got[0, 0] == 0.0 and got[0, 1] == 1.0, f"logit order: {got}"
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+
+def check_topk_bruteforce(L) -> None:
+    """With exact integer logits full of ties, the chosen set is the unique
+    k-subset S with v_i > v_j or (v_i == v_j and i < j) for every i in S,
+    j not in S; slots run in descending value, lower index first on ties."""
+    rng = np.random.default_rng(11)
+    for E, k in ((6, 2), (7, 3), (8, 4), (5, 5), (9, 1)):
+        x = rng.integers(-2, 3, size=(60, 8)).astype(np.float32)
+        wr = rng.integers(-1, 2, size=(E, 8)).astype(np.float32)
+        r = oracle.route(x, wr, None, k, "softmax", True, L=L)
+        v = (x.astype(np.int64) @ wr.astype(np.int64).T)
+        for t in range(x.shape[0]):
+            chosen = [S for S in itertools.combinations(range(E), k)
+                      if all((v[t, i] > v[t, j]) or (v[t, i] == v[t, j] and i < j)
+                             for i in S for j in range(E) if j not in S)]
+            assert len(chosen) == 1
+            got = r["idx"][t]
+            assert sorted(got.tolist()) == list(chosen[0]), f"top-k set, token {t}: {got} vs {chosen[0]}"
+            for a, b in zip(got[:-1], got[1:]):
+                assert v[t, a] > v[t, b] or (v[t, a] == v[t, b] and a < b), f"slot order, token {t}: {got}"
+
+
+def check_topk_lexsort(L) -> None:
+    """On a real-valued layer the slots equal np.lexsort by (-v, index)."""
+    for score in ("softmax", "sigmoid"):
+        cfg, inp = small_layer(T=200, d=64, E=32, k=4, score=score)
+        r = oracle.route(inp["x"], inp["w_router"], None, 4, score, True, L=L)
+        lg = r["logits"]
+        E = lg.shape[1]
+        for t in range(lg.shape[0]):
+            order = np.lexsort((np.arange(E), -lg[t].astype(np.float64)))[:4]
+            assert np.array_equal(order, r["idx"][t]), f"token {t}"
+
+
+# ---------------------------------------------------------------------------
+# weights
+# ---------------------------------------------------------------------------
+
+def check_weights(L) -> None:
+    """Renormalised weights sum to one (within k ulp); softmax weights are the
+    softmax of the selected logits; k = E gives the full softmax; k = 1 gives
+    1 (softmax) and s / (s + 1e-9) (sigmoid); without renormalisation the
+    weights are the scores themselves."""
+    for score in ("softmax", "sigmoid"):
+        for k in (1, 2, 4):
+            cfg, inp = small_layer(T=128, d=64, E=8, k=k, score=score, bias_range=0.3)
+            r = oracle.route(inp["x"], inp["w_router"], inp["sel_bias"], k, score, True, L=L)
+            w = r["w"].astype(np.float64)
+            assert np.all(np.abs(w.sum(1) - 1.0) <= k * 2 ** -23), f"{score} k={k}: sum {w.sum(1)}"
+            sel = np.take_along_axis(r["logits"].astype(np.float64), r["idx"], 1)
+            if score == "softmax":
+                ref = np.exp(sel - sel.max(1, keepdims=True))
+                ref /= ref.sum(1, keepdims=True)
+            else:
+                s = 1.0 / (1.0 + np.exp(-sel))
+                ref = s / (s.sum(1, keepdims=True) + 1e-9)
+            assert np.allclose(w, ref, rtol=1e-6, atol=0), f"{score} k={k}: weights"
+            if k == 1 and score == "softmax":
+                assert np.all(r["w"] == 1.0)
+    # k = E: full softmax over all experts
+    cfg, inp = small_layer(T=64, d=64, E=8, k=8)
+    r = oracle.route(inp["x"], inp["w_router"], None, 8, "softmax", True, L=L)
+    lg = r["logits"].astype(np.float64)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    assert np.allclose(r["w"], np.take_along_axis(p, r["idx"], 1), rtol=1e-6, atol=0)
+    # no renormalisation: the unbiased score of each chosen expert
+    for score in ("softmax", "sigmoid"):
+        cfg, inp = small_layer(T=64, d=64, E=8, k=2, score=score, bias_range=0.3)
+        r = oracle.route(inp["x"], inp["w_router"], inp["sel_bias"], 2, score, False, L=L)
+        lg = r["logits"].astype(np.float64)
+        if score == "softmax":
+            p = np.exp(lg - lg.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+        else:
+            p = 1.0 / (1.0 + np.exp(-lg))
+        assert np.allclose(r["w"], np.take_along_axis(p, r["idx"], 1), rtol=1e-6, atol=0), score
+
+
+def check_bias_selection_only(L) -> None:
+    """A +10 bias on one expert puts it in slot 0 of every token (scores lie in
+    [0, 1]) while its weight stays the renormalised unbiased score; wherever
+    the biased and unbiased selections agree slot by slot the weights are
+    bitwise equal; a biased selection equals the brute-force order of
+    fp64 score + bias where the fp64 gap is wide."""
+    for score in ("sigmoid", "softmax"):
+        cfg, inp = small_layer(T=256, d=64, E=16, k=4, score=score, bias_range=0.2)
+        x, wr, b = inp["x"], inp["w_router"], inp["sel_bias"]
+        plain = oracle.route(x, wr, None, 4, score, True, L=L)
+        biased = oracle.route(x, wr, b, 4, score, True, L=L)
+        lg = plain["logits"].astype(np.float64)
+        if score == "sigmoid":
+            s = 1.0 / (1.0 + np.exp(-lg))
+        else:
+            s = np.exp(lg - lg.max(1, keepdims=True))
+            s /= s.sum(1, keepdims=True)
+        v = s + b.astype(np.float64)
+        srt = np.sort(v, 1)[:, ::-1]
+        wide = (srt[:, 3] - srt[:, 4]) > 1e-5
+        for t in np.nonzero(wide)[0]:
+            assert set(biased["idx"][t].tolist()) == set(np.argsort(-v[t], kind="stable")[:4].tolist()), t
+        # a small bias leaves many tokens' selections unchanged and moves others
+        small = oracle.route(x, wr, (b * np.float32(0.05)).astype(np.float32), 4, score, True, L=L)
+        same = np.all(plain["idx"] == small["idx"], 1)
+        assert same.any() and (~same).any()
+        assert np.array_equal(plain["w"][same], small["w"][same])
+        # weights of the biased selection come from the unbiased scores
+        sel = np.take_along_axis(lg, biased["idx"], 1)
+        if score == "sigmoid":
+            ss = 1.0 / (1.0 + np.exp(-sel))
+            ref = ss / (ss.sum(1, keepdims=True) + 1e-9)
+        else:
+            ref = np.exp(sel - sel.max(1, keepdims=True))
+            ref /= ref.sum(1, keepdims=True)
+        assert np.allclose(biased["w"], ref, rtol=1e-6, atol=0)
+        # forcing one expert
+        force = np.zeros_like(b)
+        force[5] = 10.0
+        f = oracle.route(x, wr, force, 4, score, True, L=L)
+        assert np.all(f["idx"][:, 0] == 5)
+        sel = np.take_along_axis(lg, f["idx"], 1)
+        if score == "sigmoid":
+            ss = 1.0 / (1.0 + np.exp(-sel))
+            ref = ss / (ss.sum(1, keepdims=True) + 1e-9)
+        else:
+            ref = np.exp(sel - sel.max(1, keepdims=True))
+            ref /= ref.sum(1, keepdims=True)
+        assert np.allclose(f["w"], ref, rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# counts and dispatch
+# ---------------------------------------------------------------------------
+
+def check_dispatch(L) -> None:
+    """Counts sum to T*k, no count exceeds T (so max/mean load <= E/k), every
+    token holds k distinct experts, and row_of is the inverse of a stable
+    argsort of the flattened expert ids."""
+    cfg, inp = small_layer(T=300, d=64, E=12, k=3, score="sigmoid", bias_range=0.5)
+    r = oracle.route(inp["x"], inp["w_router"], inp["sel_bias"], 3, "sigmoid", True, L=L)
+    T, k, E = 300, 3, 12
+    assert r["counts"].sum() == T * k and r["counts"].max() <= T
+    assert np.array_equal(r["counts"], np.bincount(r["idx"].ravel(), minlength=E))
+    assert all(len(set(row)) == k for row in r["idx"].tolist())
+    assert r["counts"].max() / (T * k / E) <= E / k
+    force = np.zeros(E, np.float32)
+    force[0] = 10.0
+    f = oracle.route(inp["x"], inp["w_router"], force, 3, "sigmoid", True, L=L)
+    assert f["counts"][0] == T and np.array_equal(f["counts"], np.bincount(f["idx"].ravel(), minlength=E))
+    dsp = oracle.dispatch(r["idx"], E, L=L)
+    assert np.array_equal(dsp["counts"], r["counts"])
+    assert np.array_equal(dsp["offsets"], np.concatenate([[0], np.cumsum(r["counts"])]))
+    perm = np.argsort(r["idx"].ravel(), kind="stable")
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    assert np.array_equal(dsp["row_of"].ravel(), inv)
+
+
+# ---------------------------------------------------------------------------
+# expert math and the whole layer
+# ---------------------------------------------------------------------------
+
+def check_dense_masked(L) -> None:
+    """The routed output equals a per-token dense reference that runs all E
+    experts (numpy fp64 matmul) and masks the unselected ones, plus the shared
+    expert; checked for fp32 and bf16 inputs and both scores."""
+    for dtype, score, shared in (("f32", "softmax", False), ("bf16", "sigmoid", True), ("bf16", "softmax", True)):
+        cfg, inp = small_layer(T=70, d=64, E=6, k=2, d_ff=80, dtype=dtype, score=score, shared=shared,
+                               bias_range=0.2 if score == "sigmoid" else 0.0)
+        out = oracle.forward(inp, 2, score, True, L=L)
+        x64 = widen(inp["x"])
+        ref = np.zeros((70, 64))
+        for e in range(6):
+            ye = swiglu64(x64, inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+            mask = (out["idx"] == e)
+            coef = (out["w"].astype(np.float64) * mask).sum(1)
+            ref += coef[:, None] * ye
+        if shared:
+            ref += swiglu64(x64, inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+        err = np.abs(out["y"] - ref).max() / np.sqrt(np.mean(ref ** 2))
+        assert err < 1e-12, f"{dtype}/{score}: dense-masked mismatch {err:.3e}"
+
+
+def check_dense_swiglu(L) -> None:
+    """E = 1, k = 1: the layer is a plain SwiGLU FFN with weight 1, and a token
+    subset gives the same rows as the full layer."""
+    cfg, inp = small_layer(T=50, d=64, E=1, k=1, d_ff=112, dtype="f32")
+    out = oracle.forward(inp, 1, "softmax", True, L=L)
+    assert np.all(out["w"] == 1.0) and np.all(out["idx"] == 0)
+    ref = swiglu64(widen(inp["x"]), inp["w_gate"][0], inp["w_up"][0], inp["w_down"][0])
+    assert np.abs(out["y"] - ref).max() <= 1e-12 * np.abs(ref).max()
+    sub = np.array([49, 3, 17], np.int64)
+    out2 = oracle.forward(inp, 1, "softmax", True, tokens=sub, L=L)
+    assert np.array_equal(out2["y"], out["y"][sub])
+
+
+ALL_CHECKS = [check_cexpf, check_logits, check_topk_bruteforce, check_topk_lexsort, check_weights,
+              check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu]

@@ -1,0 +1,51 @@
+"""Planted mistakes: each test builds a copy of the oracle with one plausible
+error (a dropped term, a wrong sign or index, a transposed operand, a broken
+tie-break) and shows that at least one pin rejects it. The real oracle source
+is never modified; the copies live in a temporary directory."""
+import os
+
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+MUTANTS = {
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "tie_break_high_index": ("if (best < 0 || v[e] > v[best])", "if (best < 0 || v[e] >= v[best])"),
+    "down_weight_transposed": ("wd_off + (size_t)c * d_ff + f", "wd_off + (size_t)f * d + c"),
+    "sigmoid_bias_dropped": ("v[e] = sigmoidf_canon(l[e]) + bias[e];", "v[e] = sigmoidf_canon(l[e]);"),
+    "weights_from_biased_values": ("w[j] = sigmoidf_canon(l[idx[j]]);", "w[j] = v[idx[j]];"),
+    "logit_chain_descending": ("for (jj = 0; jj < d; jj++) {", "for (jj = d - 1; jj >= 0; jj--) {"),
+    "exp_taylor_term_dropped": ("p = fmaf(p, r, C4);", "p = fmaf(p, r, 0.0f);"),
+    "exp_reduction_sign": ("r = fmaf(-n, LN2_LO, r);", "r = fmaf(n, LN2_LO, r);"),
+    "shared_expert_dropped": ("acc += s[(size_t)i * d + c];", "acc += 0.0;"),
+    "dispatch_unstable": ("row_of[t * k + j] = offsets[e] + cursor[e]++;",
+                          "row_of[t * k + j] = offsets[e + 1] - 1 - cursor[e]++;"),
+    "renorm_sum_drops_slot": ("                s += w[j];\n            }\n            for (j = 0; j < k; j++)\n"
+                              "                w[j] = w[j] / s;",
+                              "                s += j ? w[j] : 0.0f;\n            }\n            for (j = 0; j < k; j++)\n"
+                              "                w[j] = w[j] / s;"),
+    "softmax_bias_on_logits": ("v[e] = oracle_cexpf(l[e] - m) / z + bias[e];", "v[e] = l[e] + bias[e];"),
+    "gate_up_swapped_roles": ("hb[(size_t)f * PAIR_BLOCK + b] = silu(g[b]) * u[b];",
+                              "hb[(size_t)f * PAIR_BLOCK + b] = silu(u[b]) * g[b];"),
+    "count_off_by_one": ("        counts[idx[t]]++;\n    if (!logits_out)",
+                         "        counts[idx[t] == 0 ? 1 : idx[t]]++;\n    if (!logits_out)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = os.path.join(tmp_path, f"oracle_{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(path, os.path.join(tmp_path, f"liboracle_{name}.so")))
+    failures = []
+    for check in oc.ALL_CHECKS:
+        try:
+            check(lib)
+        except AssertionError as e:
+            failures.append(f"{check.__name__}: {str(e)[:80]}")
+    assert failures, f"mutant {name} passed every pin"
