@@ -1,0 +1,215 @@
+/*
+ * moe.h — C ABI of libmoe.so: the forward pass of one Mixture-of-Experts FFN
+ * layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (moe-200m-qwen3-100b README, "Architecture diagram" and
+ * "SigmoidRouter"; SpecForge PR #930, "What this adds"):
+ *   1. router, always in fp32 (README, "Per-layer numerics"):
+ *        logits = x W_r^T; scores = sigmoid(logits) or softmax over all
+ *        experts; an optional per-expert bias is added to the scores for
+ *        the choice of experts only; top-k by descending value; combine
+ *        weights are the unbiased scores of the chosen experts, divided by
+ *        their sum (plus 1e-9 for sigmoid) when renormalising;
+ *        counts[e] = tokens that chose expert e;
+ *   2. dispatch of the (token, slot) pairs into expert-contiguous order;
+ *   3. SwiGLU experts on their rows, weights stacked [E, out, in]
+ *        (PR #930, "Why FSDP is enough here"): h = silu(x W_gate[e]^T) *
+ *        (x W_up[e]^T), out = h W_down[e]^T; the names w1 / w3 / w2 of the
+ *        pages' per-expert checkpoint keys are gate / up / down;
+ *      plus an optional shared expert that every token uses with weight 1;
+ *   4. combine back to token order: y[t] = sum_j w[t,j] out_{e_j}(x_t)
+ *        (+ shared(x_t)).
+ *
+ * Determinism. Expert ids, counts, dispatch order and combine weights are
+ * bit-reproducible: the gate product is one fp32 fma chain per (token,
+ * expert) over features in ascending order; exp inside the router is a fixed
+ * sequence of IEEE operations; ties go to the lower expert id; rows of one
+ * expert are ordered by token id. Outputs are bitwise repeatable from call to
+ * call (no floating-point atomics anywhere).
+ *
+ * Conventions for every entry point.
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them. Size out-parameters are
+ *     host pointers.
+ *   - Tensors are row-major and contiguous. bf16 data is stored as 16-bit
+ *     bf16 bit patterns; fp32 as IEEE binary32.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream). Calls return after enqueueing; none synchronises the stream,
+ *     except moe_timing_read.
+ *   - Arguments are validated before anything is enqueued; an invalid call
+ *     returns a status other than MOE_OK and leaves every buffer untouched.
+ *     MOE_ERR_HIP reports a launch error; faults inside kernels surface at
+ *     the caller's next synchronisation.
+ *   - Outputs must not alias inputs. Scratch space comes from the caller's
+ *     workspace `ws` of `ws_bytes` bytes (256-byte aligned); its contents
+ *     after a call are unspecified.
+ *   - No exception crosses this interface. Calls on different streams with
+ *     different workspaces may run concurrently.
+ */
+#ifndef MOE_MI355X_MOE_H
+#define MOE_MI355X_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* null required pointer, k < 1, k > E, T < 0, inconsistent shared expert, ... */
+    MOE_ERR_UNSUPPORTED = 2, /* d_model or d_ff not a multiple of 64, E > 1024, k > 32, unknown dtype/score */
+    MOE_ERR_WORKSPACE = 3,   /* ws_bytes below the size the matching *_workspace_size query returns */
+    MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+/* dtype of x, of the expert weights and of the internal SwiGLU activations.
+ * The router weight and the selection bias are fp32 in every case. */
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/* router score */
+#define MOE_SOFTMAX 0 /* softmax over all experts (SpecForge PR #930, qwen3 preset) */
+#define MOE_SIGMOID 1 /* sigmoid per expert (README, "SigmoidRouter") */
+
+/* One MoE FFN layer: shapes, recipe and device pointers to its weights.
+ * The counterpart of the pages' MoEModelConfig (README, "Config") restricted
+ * to the fields of one layer. Stating the shared expert inconsistently (some
+ * but not all of its three weights, or a width without weights) is an error,
+ * as conflicting statements of the expert count are on the pages
+ * (PR #930, "What this adds": num_experts vs n_routed_experts). */
+typedef struct moe_layer {
+    int32_t d_model;     /* d: features per token; multiple of 64 */
+    int32_t d_ff;        /* width of each routed expert; multiple of 64 */
+    int32_t n_experts;   /* E: routed experts, 1..1024 */
+    int32_t top_k;       /* k: experts per token, 1..min(E, 32) */
+    int32_t score;       /* MOE_SOFTMAX or MOE_SIGMOID */
+    int32_t renorm;      /* nonzero: combine weights renormalised over the k chosen experts */
+    int32_t dtype;       /* MOE_F32 or MOE_BF16 */
+    int32_t d_ff_shared; /* width of the shared expert; 0 when there is none; multiple of 64 */
+    const float *w_router; /* [E, d] fp32 (nn.Linear layout) */
+    const float *sel_bias; /* [E] fp32 selection bias, or NULL; moves selection only */
+    const void *w_gate;    /* [E, d_ff, d]  (w1) */
+    const void *w_up;      /* [E, d_ff, d]  (w3) */
+    const void *w_down;    /* [E, d, d_ff]  (w2) */
+    const void *ws_gate;   /* [d_ff_shared, d] or NULL */
+    const void *ws_up;     /* [d_ff_shared, d] or NULL */
+    const void *ws_down;   /* [d, d_ff_shared] or NULL */
+} moe_layer;
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_str(moe_status s);
+
+/* Workspace bytes that moe_forward, moe_route, moe_permute and moe_combine
+ * need for this layer and T tokens (one size serves all four). */
+moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
+
+/*
+ * Router (README "SigmoidRouter"; PR #930 qwen3 preset).
+ *   x        [T, d] in layer->dtype
+ *   topk_idx [T, k] int32 out: expert ids, slot 0 has the largest selection value
+ *   topk_w   [T, k] fp32 out: combine weights
+ *   counts   [E] int32 out: tokens per expert (may be NULL)
+ * Selection value: the logit when sel_bias is NULL; otherwise the score plus
+ * the bias (sigmoid: 1/(1+exp(-l)); softmax: exp(l-m)/sum exp(l-m), summed in
+ * expert order). Weights: softmax renorm exp(l_j - M)/sum_i exp(l_i - M) over
+ * the chosen logits; sigmoid renorm s_j/(sum_i s_i + 1e-9); without renorm the
+ * score itself. T = 0 zeroes counts.
+ */
+moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, int32_t *topk_idx, float *topk_w,
+                     int32_t *counts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dispatch into expert-contiguous order ("SigmoidRouter" one-hot counts;
+ * PR #930 grouped_mm over rows grouped by expert).
+ *   x        [T, d] in layer->dtype
+ *   topk_idx [T, k] int32 in (from moe_route; every id in [0, E), the k ids of
+ *            a token distinct)
+ *   x_perm   [T*k, d] out: x_perm[row_of[t, j]] = x[t]; may be NULL
+ *   offsets  [E+1] int32 out: exclusive prefix sum of the per-expert counts
+ *   row_of   [T, k] int32 out: row of pair (t, j) in x_perm; rows of one
+ *            expert are in ascending token order
+ */
+moe_status moe_permute(const moe_layer *layer, const void *x, int64_t T, const int32_t *topk_idx, void *x_perm,
+                       int32_t *offsets, int32_t *row_of, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for moe_grouped_swiglu. */
+moe_status moe_grouped_swiglu_workspace_size(int32_t dtype, int32_t n_groups, int32_t d_in, int32_t d_ff,
+                                             int64_t rows, size_t *bytes);
+
+/*
+ * SwiGLU experts over row groups (README "Architecture diagram": SwiGLU
+ * experts; PR #930 "Why FSDP is enough here": stacked [E, out, in]).
+ *   a        [rows, d_in] in dtype; group g owns rows offsets[g]..offsets[g+1]-1
+ *   offsets  [n_groups+1] int32 DEVICE array, nondecreasing, offsets[0] = 0,
+ *            offsets[n_groups] = rows (not checked on the host: it is device data)
+ *   w_gate, w_up [n_groups, d_ff, d_in]; w_down [n_groups, d_in, d_ff]
+ *   out      [rows, d_in] fp32: W_down[g] (silu(W_gate[g] a) * (W_up[g] a))
+ * The intermediate activation is rounded to dtype (bf16 for MOE_BF16)
+ * before the down projection; accumulation is fp32.
+ */
+moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int32_t d_ff, int64_t rows,
+                              const void *a, const int32_t *offsets, const void *w_gate, const void *w_up,
+                              const void *w_down, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Weighted combine back to token order (README "Architecture diagram":
+ * weighted sum of the routed experts and the shared expert).
+ *   y_perm   [T*k, d] fp32: expert outputs in dispatch order
+ *   row_of   [T, k] int32 (from moe_permute)
+ *   topk_w   [T, k] fp32
+ *   y_shared [T, d] fp32 or NULL: added with weight 1 after the routed terms
+ *   y        [T, d] fp32 out: y[t] = sum_j topk_w[t,j] y_perm[row_of[t,j]] (+ y_shared[t]),
+ *            slots summed in order, no atomics
+ */
+moe_status moe_combine(const moe_layer *layer, int64_t T, const float *y_perm, const int32_t *row_of,
+                       const float *topk_w, const float *y_shared, float *y, void *stream);
+
+/*
+ * The whole layer: route, dispatch, routed and shared SwiGLU experts, combine.
+ *   x   [T, d] in layer->dtype
+ *   y   [T, d] fp32 out
+ *   topk_idx [T, k], topk_w [T, k], counts [E]: optional outputs (NULL: kept
+ *   in the workspace only)
+ * Routed rows are gathered from x inside the expert GEMM; no permuted copy of
+ * x is written. T = 0 zeroes counts and returns.
+ */
+moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T, float *y, int32_t *topk_idx,
+                       float *topk_w, int32_t *counts, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Phase timing (measurement only)                                         */
+/* ---------------------------------------------------------------------- */
+
+/* Phases of moe_forward, in launch order. */
+#define MOE_PHASE_ROUTE 0          /* gate product, scores, top-k, weights, block histograms */
+#define MOE_PHASE_SCAN 1           /* counts, offsets, per-block bases, GEMM tile list */
+#define MOE_PHASE_SCATTER 2        /* row_of and the row -> token map */
+#define MOE_PHASE_GATEUP 3         /* routed gate/up grouped GEMM with the SwiGLU epilogue */
+#define MOE_PHASE_DOWN 4           /* routed down grouped GEMM */
+#define MOE_PHASE_SHARED_GATEUP 5  /* shared expert gate/up (empty without one) */
+#define MOE_PHASE_SHARED_DOWN 6    /* shared expert down (empty without one) */
+#define MOE_PHASE_COMBINE 7        /* weighted combine */
+#define MOE_N_PHASES 8
+
+typedef struct moe_timing moe_timing; /* opaque: one hipEvent per phase boundary */
+
+/* Create / destroy a timing record (creates hipEvents on the current device). */
+moe_status moe_timing_create(moe_timing **out);
+moe_status moe_timing_destroy(moe_timing *t);
+
+/* moe_forward, recording an event on `stream` at every phase boundary. */
+moe_status moe_forward_timed(const moe_layer *layer, const void *x, int64_t T, float *y, int32_t *topk_idx,
+                             float *topk_w, int32_t *counts, void *ws, size_t ws_bytes, void *stream,
+                             moe_timing *t);
+
+/* Milliseconds spent in each phase by the last moe_forward_timed call that
+ * used `t`; waits for its events. phase_ms: host array of MOE_N_PHASES. */
+moe_status moe_timing_read(moe_timing *t, float *phase_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_MOE_H */

@@ -1,0 +1,61 @@
+// Weighted combine back to token order (moe-200m-qwen3-100b README,
+// "Architecture diagram": routed experts and the always-on shared expert feed
+// one weighted sum).
+//   y[t] = sum_{j<k} w[t,j] * Y[row_of[t,j]]  (+ S[t], weight 1, added last)
+// A gather: one wave per token reads its k expert rows and writes its output
+// row once, in fp32, slots in order. No atomics, so the result is the same
+// bits on every run.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const float* __restrict__ y_perm,
+                                                 const int32_t* __restrict__ row_of, const float* __restrict__ w,
+                                                 const float* __restrict__ y_shared, float* __restrict__ y) {
+  __shared__ int rows_s[4][32];
+  __shared__ float w_s[4][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  const bool valid = t < T;
+  if (valid && lane < k) {
+    rows_s[wave][lane] = row_of[t * k + lane];
+    w_s[wave][lane] = w[t * k + lane];
+  }
+  __syncthreads();
+  if (!valid) return;
+  const int n4 = d >> 2;
+  const int64_t n_rows = T * k;
+  const f32x4* Y = reinterpret_cast<const f32x4*>(y_perm);
+  for (int c = lane; c < n4; c += 64) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = rows_s[wave][j];
+      if (r < 0 || r >= n_rows) continue;  // invalid row ids contribute nothing
+      const f32x4 v = Y[(size_t)r * n4 + c];
+      const float wj = w_s[wave][j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wj, v[q], acc[q]);
+    }
+    if (y_shared) {
+      const f32x4 sv = reinterpret_cast<const f32x4*>(y_shared)[(size_t)t * n4 + c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += sv[q];
+    }
+    reinterpret_cast<f32x4*>(y)[(size_t)t * n4 + c] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const int32_t* row_of, const float* w,
+                          const float* y_shared, float* y, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (k > 32 || (d & 3)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared,
+                     y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,72 @@
+// Host-side launch interface of the HIP kernels (internal to libmoe.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ router
+struct RouteLaunch {
+  const void* x;         // [T, d] fp32 or bf16 bits
+  int dtype;             // 0 fp32, 1 bf16
+  int64_t T;
+  int d, E, k, score, renorm;
+  const float* w_router;  // [E, d]
+  const float* bias;      // [E] or null
+  int32_t* idx;           // [T, k]
+  float* w;               // [T, k]
+  int32_t* hist;          // [n_blocks, E] or null
+  int32_t* rank;          // [T, k] or null (needs hist)
+};
+int route_tokens_per_block(int E);
+size_t route_lds_bytes(int E, int k);
+hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+
+// --------------------------------------------------------------- dispatch
+// Per-block expert histograms and ranks from expert ids (no routing).
+int hist_tokens_per_block();
+hipError_t launch_hist_rank(const int32_t* idx, int64_t T, int k, int E, int32_t* hist, int32_t* rank,
+                            hipStream_t s);
+// counts[e] = sum over blocks of hist[b, e].
+hipError_t launch_counts(const int32_t* hist, int nb, int E, int32_t* counts, hipStream_t s);
+// counts, offsets [E+1], per-block bases [nb, E], and the tile list of a
+// grouped GEMM with row tile bm: tiles[i] = (group, m-tile), n_tiles[0] = count.
+hipError_t launch_scan(const int32_t* hist, int nb, int E, int32_t* counts, int32_t* offsets, int32_t* base, int bm,
+                       int32_t* n_tiles, int2* tiles, hipStream_t s);
+// Tile list from device offsets [G+1].
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int G, int bm, int32_t* n_tiles, int2* tiles,
+                                     hipStream_t s);
+// row_of [T, k], tok_of_row [T*k] and optionally x_perm rows.
+hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* base, int64_t T, int k, int E,
+                          int tokens_per_block, int32_t* row_of, int32_t* tok_of_row, const void* x, void* x_perm,
+                          int row_bytes, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// ------------------------------------------------------------------- GEMM
+struct GemmLaunch {
+  int dtype;               // 0 fp32, 1 bf16 (operands; accumulation fp32)
+  bool gateup;             // true: out = silu(A B0^T) * (A B1^T) in dtype; false: out = A B0^T in fp32
+  const void* a;           // rows of K elements
+  const int32_t* a_rows;   // null, or the source row of a for every grouped row (gather)
+  int64_t a_row_count;     // rows of a (gather indices are clamped into range)
+  int n_groups;            // G (tile entries naming another group are skipped)
+  const void* b0;          // [G, N, K]
+  const void* b1;          // [G, N, K] (gateup)
+  void* out;               // [rows, N]
+  int N, K;
+  // grouped mode: tile list from launch_scan / launch_tiles_from_offsets
+  const int32_t* offsets;  // [G+1] or null for one dense group of `rows` rows
+  const int2* tiles;
+  const int32_t* n_tiles;
+  int64_t max_m_tiles;     // grid bound on m-tiles
+  int64_t rows;            // dense mode: number of rows
+};
+int gemm_bm(int dtype, bool gateup);
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const int32_t* row_of, const float* w,
+                          const float* y_shared, float* y, hipStream_t s);
+
+}  // namespace moe

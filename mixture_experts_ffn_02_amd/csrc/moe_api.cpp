@@ -1,0 +1,421 @@
+// C ABI of libmoe.so: argument validation, workspace layout and the launch
+// sequence of the MoE FFN layer forward pass. Declarations and the contract
+// of every entry point are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+// Checks of a layer description that do not depend on T.
+moe_status check_layer(const moe_layer* L, bool need_experts) {
+  if (!L) return MOE_ERR_INVALID;
+  if (L->dtype != MOE_F32 && L->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (L->score != MOE_SOFTMAX && L->score != MOE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (L->d_model <= 0 || L->d_ff <= 0 || L->n_experts <= 0 || L->d_ff_shared < 0) return MOE_ERR_INVALID;
+  if (L->top_k < 1 || L->top_k > L->n_experts) return MOE_ERR_INVALID;
+  if (L->d_model % 64 || L->d_ff % 64 || L->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
+  if (L->n_experts > 1024 || L->top_k > 32) return MOE_ERR_UNSUPPORTED;
+  if (!L->w_router || !aligned16(L->w_router)) return MOE_ERR_INVALID;
+  // The shared expert is stated by all three weights and a width, or by none.
+  const int n_shared = (L->ws_gate != nullptr) + (L->ws_up != nullptr) + (L->ws_down != nullptr);
+  if (n_shared != 0 && n_shared != 3) return MOE_ERR_INVALID;
+  if ((n_shared == 3) != (L->d_ff_shared > 0)) return MOE_ERR_INVALID;
+  if (n_shared == 3 && (!aligned16(L->ws_gate) || !aligned16(L->ws_up) || !aligned16(L->ws_down)))
+    return MOE_ERR_INVALID;
+  if (need_experts) {
+    if (!L->w_gate || !L->w_up || !L->w_down) return MOE_ERR_INVALID;
+    if (!aligned16(L->w_gate) || !aligned16(L->w_up) || !aligned16(L->w_down)) return MOE_ERR_INVALID;
+  }
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, h, yperm, hs, ys, total;
+  int64_t nb;         // histogram rows (blocks)
+  int64_t max_tiles;  // bound on grouped GEMM row tiles
+};
+
+// One layout serves moe_forward, moe_route, moe_permute and moe_combine.
+Layout make_layout(const moe_layer* L, int64_t T) {
+  Layout o{};
+  const int64_t E = L->n_experts, k = L->top_k, d = L->d_model, f = L->d_ff, fs = L->d_ff_shared;
+  const int64_t rows = T * k;
+  const int eb = elem_bytes(L->dtype);
+  const int64_t tpb_r = route_tokens_per_block((int)E), tpb_h = hist_tokens_per_block();
+  const int64_t tpb = tpb_r < tpb_h ? tpb_r : tpb_h;
+  o.nb = (T + tpb - 1) / tpb;
+  const int bm = gemm_bm(L->dtype, true);
+  o.max_tiles = (rows + bm - 1) / bm + E;
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p = align_up(p + bytes);
+    return at;
+  };
+  o.hist = take(sizeof(int32_t) * (size_t)(o.nb * E));
+  o.base = take(sizeof(int32_t) * (size_t)(o.nb * E));
+  o.rank = take(sizeof(int32_t) * (size_t)rows);
+  o.counts = take(sizeof(int32_t) * (size_t)E);
+  o.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+  o.n_tiles = take(sizeof(int32_t));
+  o.tiles = take(sizeof(int2) * (size_t)o.max_tiles);
+  o.row_of = take(sizeof(int32_t) * (size_t)rows);
+  o.tok_of_row = take(sizeof(int32_t) * (size_t)rows);
+  o.idx = take(sizeof(int32_t) * (size_t)rows);
+  o.w = take(sizeof(float) * (size_t)rows);
+  o.h = take((size_t)eb * (size_t)(rows * f));
+  o.yperm = take(sizeof(float) * (size_t)(rows * d));
+  o.hs = take((size_t)eb * (size_t)(T * fs));
+  o.ys = take(sizeof(float) * (size_t)(fs > 0 ? T * d : 0));
+  o.total = p;
+  return o;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<unsigned char*>(ws) + off);
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                \
+  do {                                               \
+    const hipError_t moe_e_ = (expr);                \
+    if (moe_e_ != hipSuccess) return MOE_ERR_HIP;    \
+  } while (0)
+
+}  // namespace
+
+struct moe_timing {
+  hipEvent_t ev[MOE_N_PHASES + 1];
+};
+
+namespace {
+
+void mark(moe_timing* t, int i, hipStream_t s) {
+  if (t) (void)hipEventRecord(t->ev[i], s);
+}
+
+moe_status check_T(int64_t T, int k) {
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T * (int64_t)k > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* idx, float* w,
+                        int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s, moe_timing* tm) {
+  moe_status st = check_layer(L, true);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if (T > 0 && (!x || !y || !aligned16(x) || !aligned16(y))) return MOE_ERR_INVALID;
+  if ((idx && !aligned16(idx)) || (w && !aligned16(w))) return MOE_ERR_INVALID;
+  const Layout lo = make_layout(L, T);
+  if (T > 0 && (!ws || ws_bytes < lo.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  if (T == 0) {
+    for (int i = 0; i <= MOE_N_PHASES; ++i) mark(tm, i, s);
+    if (counts) MOE_TRY(launch_fill_i32(counts, L->n_experts, 0, s));
+    return MOE_OK;
+  }
+  const int E = L->n_experts, k = L->top_k, d = L->d_model;
+  int32_t* idx_p = idx ? idx : at<int32_t>(ws, lo.idx);
+  float* w_p = w ? w : at<float>(ws, lo.w);
+  int32_t* counts_p = counts ? counts : at<int32_t>(ws, lo.counts);
+  int32_t* hist = at<int32_t>(ws, lo.hist);
+  int32_t* rank = at<int32_t>(ws, lo.rank);
+  int32_t* base = at<int32_t>(ws, lo.base);
+  int32_t* offsets = at<int32_t>(ws, lo.offsets);
+  int32_t* n_tiles = at<int32_t>(ws, lo.n_tiles);
+  int2* tiles = at<int2>(ws, lo.tiles);
+  int32_t* row_of = at<int32_t>(ws, lo.row_of);
+  int32_t* tok_of_row = at<int32_t>(ws, lo.tok_of_row);
+  const int bm = gemm_bm(L->dtype, true);
+  const int tpb = route_tokens_per_block(E);
+  const int64_t nb_route = (T + tpb - 1) / tpb;
+
+  mark(tm, MOE_PHASE_ROUTE, s);
+  RouteLaunch r{x, L->dtype, T, d, E, k, L->score, L->renorm, L->w_router, L->sel_bias, idx_p, w_p, hist, rank};
+  MOE_TRY(launch_route(r, s));
+  mark(tm, MOE_PHASE_SCAN, s);
+  MOE_TRY(launch_scan(hist, (int)nb_route, E, counts_p, offsets, base, bm, n_tiles, tiles, s));
+  mark(tm, MOE_PHASE_SCATTER, s);
+  MOE_TRY(launch_scatter(idx_p, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s));
+
+  mark(tm, MOE_PHASE_GATEUP, s);
+  GemmLaunch gu{};
+  gu.dtype = L->dtype;
+  gu.gateup = true;
+  gu.a = x;
+  gu.a_rows = tok_of_row;
+  gu.a_row_count = T;
+  gu.n_groups = E;
+  gu.b0 = L->w_gate;
+  gu.b1 = L->w_up;
+  gu.out = at<void>(ws, lo.h);
+  gu.N = L->d_ff;
+  gu.K = d;
+  gu.offsets = offsets;
+  gu.tiles = tiles;
+  gu.n_tiles = n_tiles;
+  gu.max_m_tiles = lo.max_tiles;
+  MOE_TRY(launch_gemm(gu, s));
+  mark(tm, MOE_PHASE_DOWN, s);
+  GemmLaunch dn = gu;
+  dn.gateup = false;
+  dn.a = at<void>(ws, lo.h);
+  dn.a_rows = nullptr;
+  dn.b0 = L->w_down;
+  dn.b1 = nullptr;
+  dn.out = at<void>(ws, lo.yperm);
+  dn.N = d;
+  dn.K = L->d_ff;
+  MOE_TRY(launch_gemm(dn, s));
+
+  const float* shared_out = nullptr;
+  mark(tm, MOE_PHASE_SHARED_GATEUP, s);
+  if (L->d_ff_shared > 0) {
+    GemmLaunch sg{};
+    sg.dtype = L->dtype;
+    sg.gateup = true;
+    sg.a = x;
+    sg.b0 = L->ws_gate;
+    sg.b1 = L->ws_up;
+    sg.out = at<void>(ws, lo.hs);
+    sg.N = L->d_ff_shared;
+    sg.K = d;
+    sg.rows = T;
+    MOE_TRY(launch_gemm(sg, s));
+  }
+  mark(tm, MOE_PHASE_SHARED_DOWN, s);
+  if (L->d_ff_shared > 0) {
+    GemmLaunch sd{};
+    sd.dtype = L->dtype;
+    sd.gateup = false;
+    sd.a = at<void>(ws, lo.hs);
+    sd.b0 = L->ws_down;
+    sd.out = at<void>(ws, lo.ys);
+    sd.N = d;
+    sd.K = L->d_ff_shared;
+    sd.rows = T;
+    MOE_TRY(launch_gemm(sd, s));
+    shared_out = at<float>(ws, lo.ys);
+  }
+  mark(tm, MOE_PHASE_COMBINE, s);
+  MOE_TRY(launch_combine(T, d, k, at<float>(ws, lo.yperm), row_of, w_p, shared_out, y, s));
+  mark(tm, MOE_N_PHASES, s);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or option not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_workspace_size(const moe_layer* L, int64_t T, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID;
+  moe_status st = check_layer(L, false);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  *bytes = make_layout(L, T).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer* L, const void* x, int64_t T, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_layer(L, false);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if (T > 0 && (!x || !topk_idx || !topk_w || !aligned16(x))) return MOE_ERR_INVALID;
+  const Layout lo = make_layout(L, T);
+  if (T > 0 && counts && (!ws || ws_bytes < lo.total)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (T == 0) {
+    if (counts) MOE_TRY(launch_fill_i32(counts, L->n_experts, 0, s));
+    return MOE_OK;
+  }
+  int32_t* hist = counts ? at<int32_t>(ws, lo.hist) : nullptr;
+  RouteLaunch r{x, L->dtype, T, L->d_model, L->n_experts, L->top_k, L->score, L->renorm, L->w_router,
+                L->sel_bias, topk_idx, topk_w, hist, nullptr};
+  MOE_TRY(launch_route(r, s));
+  if (counts) {
+    const int tpb = route_tokens_per_block(L->n_experts);
+    MOE_TRY(launch_counts(hist, (int)((T + tpb - 1) / tpb), L->n_experts, counts, s));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_layer* L, const void* x, int64_t T, const int32_t* topk_idx, void* x_perm,
+                       int32_t* offsets, int32_t* row_of, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_layer(L, false);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if (!offsets) return MOE_ERR_INVALID;
+  if (T > 0 && (!topk_idx || !row_of)) return MOE_ERR_INVALID;
+  if (T > 0 && x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID;
+  const Layout lo = make_layout(L, T);
+  if (!ws || ws_bytes < lo.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int E = L->n_experts, k = L->top_k;
+  if (T == 0) {
+    MOE_TRY(launch_fill_i32(offsets, E + 1, 0, s));
+    return MOE_OK;
+  }
+  const int tpb = hist_tokens_per_block();
+  const int64_t nb = (T + tpb - 1) / tpb;
+  int32_t* hist = at<int32_t>(ws, lo.hist);
+  int32_t* rank = at<int32_t>(ws, lo.rank);
+  int32_t* base = at<int32_t>(ws, lo.base);
+  MOE_TRY(launch_hist_rank(topk_idx, T, k, E, hist, rank, s));
+  MOE_TRY(launch_scan(hist, (int)nb, E, at<int32_t>(ws, lo.counts), offsets, base, gemm_bm(L->dtype, true),
+                      at<int32_t>(ws, lo.n_tiles), at<int2>(ws, lo.tiles), s));
+  MOE_TRY(launch_scatter(topk_idx, rank, base, T, k, E, tpb, row_of, at<int32_t>(ws, lo.tok_of_row), x, x_perm,
+                         L->d_model * elem_bytes(L->dtype), s));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_swiglu_workspace_size(int32_t dtype, int32_t n_groups, int32_t d_in, int32_t d_ff,
+                                             int64_t rows, size_t* bytes) {
+  if (!bytes || n_groups < 1 || d_in <= 0 || d_ff <= 0 || rows < 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d_in % 64 || d_ff % 64) return MOE_ERR_UNSUPPORTED;
+  if (rows > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  const int bm = gemm_bm(dtype, true);
+  const int64_t max_tiles = (rows + bm - 1) / bm + n_groups;
+  size_t p = align_up(sizeof(int32_t));
+  p += align_up(sizeof(int2) * (size_t)max_tiles);
+  p += align_up((size_t)elem_bytes(dtype) * (size_t)rows * (size_t)d_ff);
+  *bytes = p;
+  return MOE_OK;
+}
+
+moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int32_t d_ff, int64_t rows,
+                              const void* a, const int32_t* offsets, const void* w_gate, const void* w_up,
+                              const void* w_down, float* out, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  moe_status st = moe_grouped_swiglu_workspace_size(dtype, n_groups, d_in, d_ff, rows, &need);
+  if (st != MOE_OK) return st;
+  if (!offsets || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down)) return MOE_ERR_INVALID;
+  if (rows > 0 && (!a || !out || !aligned16(a) || !aligned16(out))) return MOE_ERR_INVALID;
+  if (rows == 0) return MOE_OK;
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int bm = gemm_bm(dtype, true);
+  const int64_t max_tiles = (rows + bm - 1) / bm + n_groups;
+  int32_t* n_tiles = at<int32_t>(ws, 0);
+  int2* tiles = at<int2>(ws, align_up(sizeof(int32_t)));
+  void* h = at<void>(ws, align_up(sizeof(int32_t)) + align_up(sizeof(int2) * (size_t)max_tiles));
+  MOE_TRY(launch_tiles_from_offsets(offsets, n_groups, bm, n_tiles, tiles, s));
+  GemmLaunch gu{};
+  gu.dtype = dtype;
+  gu.gateup = true;
+  gu.a = a;
+  gu.b0 = w_gate;
+  gu.b1 = w_up;
+  gu.out = h;
+  gu.N = d_ff;
+  gu.K = d_in;
+  gu.offsets = offsets;
+  gu.tiles = tiles;
+  gu.n_tiles = n_tiles;
+  gu.max_m_tiles = max_tiles;
+  gu.n_groups = n_groups;
+  MOE_TRY(launch_gemm(gu, s));
+  GemmLaunch dn = gu;
+  dn.gateup = false;
+  dn.a = h;
+  dn.b0 = w_down;
+  dn.b1 = nullptr;
+  dn.out = out;
+  dn.N = d_in;
+  dn.K = d_ff;
+  MOE_TRY(launch_gemm(dn, s));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_layer* L, int64_t T, const float* y_perm, const int32_t* row_of,
+                       const float* topk_w, const float* y_shared, float* y, void* stream) {
+  moe_status st = check_layer(L, false);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !row_of || !topk_w || !y) return MOE_ERR_INVALID;
+  if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID;
+  (void)hipGetLastError();
+  MOE_TRY(launch_combine(T, L->d_model, L->top_k, y_perm, row_of, topk_w, y_shared, y, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(L, x, T, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_timing_create(moe_timing** out) {
+  if (!out) return MOE_ERR_INVALID;
+  moe_timing* t = new (std::nothrow) moe_timing;
+  if (!t) return MOE_ERR_HIP;
+  for (int i = 0; i <= MOE_N_PHASES; ++i) {
+    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
+      delete t;
+      return MOE_ERR_HIP;
+    }
+  }
+  *out = t;
+  return MOE_OK;
+}
+
+moe_status moe_timing_destroy(moe_timing* t) {
+  if (!t) return MOE_ERR_INVALID;
+  for (int i = 0; i <= MOE_N_PHASES; ++i) (void)hipEventDestroy(t->ev[i]);
+  delete t;
+  return MOE_OK;
+}
+
+moe_status moe_forward_timed(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, void* ws, size_t ws_bytes, void* stream,
+                             moe_timing* t) {
+  if (!t) return MOE_ERR_INVALID;
+  return forward_impl(L, x, T, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, t);
+}
+
+moe_status moe_timing_read(moe_timing* t, float* phase_ms) {
+  if (!t || !phase_ms) return MOE_ERR_INVALID;
+  if (hipEventSynchronize(t->ev[MOE_N_PHASES]) != hipSuccess) return MOE_ERR_HIP;
+  for (int i = 0; i < MOE_N_PHASES; ++i) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, t->ev[i], t->ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
+    phase_ms[i] = ms;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

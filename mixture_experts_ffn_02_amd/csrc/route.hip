@@ -1,0 +1,458 @@
+// Router kernel: fp32 gate product, scores, wavefront top-k, combine weights,
+// and the per-block expert histogram and ranks used by the dispatch.
+//
+// The layer's router runs in fp32 whatever the activation dtype
+// (moe-200m-qwen3-100b README, "Per-layer numerics"; "SigmoidRouter":
+// logits, sigmoid, bias for selection only, topk, weight gather and
+// renormalisation; SpecForge PR #930, "What this adds": softmax over all
+// experts with renormalised top-k weights).
+//
+// This file is compiled with -ffp-contract=off, IEEE division and fp32
+// denormals kept, so that every value that decides an expert id is a fixed
+// sequence of IEEE operations:
+//   * logits: one fma chain per (token, expert), features ascending, from +0;
+//   * exp: canonical_exp below (Cody-Waite reduction, Taylor degree 7);
+//   * softmax normaliser: summed over experts in ascending order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// exp(a) in fp32 from +, -, *, / and fma only.
+//  n = rint(a * log2 e); r = a - n*ln2 with ln2 = hi + lo (hi = ln2 rounded to
+//  fp32, lo = the fp32 rounding of the remainder), one fma each (Cody & Waite
+//  1980); exp(r) = Taylor series to r^7 in Horner form; scale by 2^n built
+//  from its exponent bits, in two steps when 2^n is not a normal fp32 so that
+//  only the last multiply rounds.
+__device__ __forceinline__ float canonical_exp(float a) {
+  if (a != a) return a;
+  if (a > 88.72283935546875f) return __builtin_inff();
+  if (a < -103.972084045410f) return 0.0f;
+  const float n = __builtin_rintf(a * 1.44269504088896340736f);
+  float r = __builtin_fmaf(-n, 0.693147182464599609375f, a);
+  r = __builtin_fmaf(-n, -1.9046542121259336e-09f, r);
+  float p = 1.0f / 5040.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const int ni = (int)n;
+  if (ni > 127) return (p * 2.0f) * __uint_as_float((uint32_t)(ni - 1 + 127) << 23);
+  if (ni < -126)
+    return (p * __uint_as_float((uint32_t)(ni + 64 + 127) << 23)) * __uint_as_float((uint32_t)(127 - 64) << 23);
+  return p * __uint_as_float((uint32_t)(ni + 127) << 23);
+}
+
+__device__ __forceinline__ float sigmoid_canon(float l) { return 1.0f / (1.0f + canonical_exp(-l)); }
+
+// Orderable 64-bit key: larger value first, then lower expert id.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  v = v + 0.0f;  // -0 -> +0, so that the two zeros tie
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+// Launch shape per padded expert count EP (power of two, 8..1024):
+//   ME experts x MT tokens per thread, EG expert groups x TG token groups
+//   = 256 threads, TT = TG*MT tokens per block, KC features per LDS stage.
+template <int EP>
+struct RouteShape;
+#define ROUTE_SHAPE(EP_, ME_, MT_, KC_)                        \
+  template <>                                                  \
+  struct RouteShape<EP_> {                                     \
+    static constexpr int ME = ME_, MT = MT_, KC = KC_;         \
+    static constexpr int EG = EP_ / ME_, TG = 256 / (EP_ / ME_); \
+    static constexpr int TT = (256 / (EP_ / ME_)) * MT_;       \
+  };
+ROUTE_SHAPE(8, 4, 2, 32)
+ROUTE_SHAPE(16, 4, 4, 32)
+ROUTE_SHAPE(32, 4, 8, 32)
+ROUTE_SHAPE(64, 8, 4, 32)
+ROUTE_SHAPE(128, 8, 8, 32)
+ROUTE_SHAPE(256, 8, 8, 32)
+ROUTE_SHAPE(512, 16, 4, 16)
+ROUTE_SHAPE(1024, 16, 4, 8)
+#undef ROUTE_SHAPE
+
+template <int EP>
+struct RouteLds {
+  using S = RouteShape<EP>;
+  static constexpr int kStage = 2 * S::KC * (S::TT + EP);  // floats
+  static constexpr int kLogits = S::TT * (EP + 1);          // floats
+  static constexpr int kUnion = kStage > kLogits ? kStage : kLogits;
+  static constexpr int kWords = (S::TT + 63) / 64;
+  static size_t bytes(int k) {
+    return sizeof(float) * kUnion + sizeof(uint64_t) * EP * kWords + sizeof(int) * S::TT * k +
+           sizeof(float) * (EP + 2 * S::TT);
+  }
+};
+
+template <typename XT>
+struct XLoad;
+template <>
+struct XLoad<uint16_t> {
+  static constexpr int V = 8;  // elements per 16-byte load
+  __device__ static void widen(const u32x4& r, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(r[i] << 16);
+      o[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct XLoad<float> {
+  static constexpr int V = 4;
+  __device__ static void widen(const u32x4& r, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(r[i]);
+  }
+};
+
+// Ranks of a block's (token, slot) pairs within their expert, and the block's
+// expert histogram, from the chosen ids in LDS (sel[tt*k + j]). Bit tt of
+// masks[e*W + tt/64] marks that token tt of the block chose e; the rank of
+// (tt, e) is the number of marked tokens before tt. Integer OR is order-free,
+// so the result is deterministic.
+__device__ void block_hist_rank(const int* sel, int tt_count, int k, int E, int W, uint64_t* masks,
+                                int32_t* hist_row, int32_t* rank_out) {
+  for (int q = threadIdx.x; q < tt_count * k; q += blockDim.x) {
+    const int tt = q / k, e = sel[q];
+    atomicOr((unsigned long long*)&masks[e * W + (tt >> 6)], 1ull << (tt & 63));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int h = 0;
+    for (int w = 0; w < W; ++w) h += __popcll(masks[e * W + w]);
+    hist_row[e] = h;
+  }
+  if (!rank_out) return;
+  for (int q = threadIdx.x; q < tt_count * k; q += blockDim.x) {
+    const int tt = q / k, e = sel[q];
+    int r = 0;
+    for (int w = 0; w < (tt >> 6); ++w) r += __popcll(masks[e * W + w]);
+    r += __popcll(masks[e * W + (tt >> 6)] & ((1ull << (tt & 63)) - 1ull));
+    rank_out[q] = r;
+  }
+}
+
+template <int EP, typename XT>
+__global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
+  using S = RouteShape<EP>;
+  using L = RouteLds<EP>;
+  constexpr int ME = S::ME, MT = S::MT, KC = S::KC, EG = S::EG, TG = S::TG, TT = S::TT;
+  constexpr int V = XLoad<XT>::V;
+  constexpr int W = L::kWords;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  float* uni = reinterpret_cast<float*>(lds_raw);
+  uint64_t* masks = reinterpret_cast<uint64_t*>(uni + L::kUnion);
+  int* sel = reinterpret_cast<int*>(masks + EP * W);
+  float* bias_s = reinterpret_cast<float*>(sel + TT * p.k);
+  float* tok_m = bias_s + EP;
+  float* tok_z = tok_m + TT;
+
+  const int tid = threadIdx.x;
+  const int E = p.E, k = p.k, d = p.d;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int tt_count = (int)((p.T - t0) < TT ? (p.T - t0) : TT);
+  const XT* __restrict__ x = reinterpret_cast<const XT*>(p.x);
+  const float* __restrict__ wr = p.w_router;
+
+  for (int e = tid; e < EP; e += 256) bias_s[e] = (p.bias && e < E) ? p.bias[e] : 0.0f;
+  for (int q = tid; q < EP * W; q += 256) masks[q] = 0ull;
+
+  // ---- gate product: logits[tt][e] = fma chain over features ascending
+  const int tg = tid % TG, eg = tid / TG;
+  float acc[MT][ME];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
+
+  constexpr int XCH = TT * KC / V;             // 16-byte x loads per stage
+  constexpr int XPT = (XCH + 255) / 256;
+  constexpr int WCH = EP * KC / 4;             // 16-byte router-weight loads per stage
+  constexpr int WPT = (WCH + 255) / 256;
+  u32x4 xr[XPT], wreg[WPT];
+  const int nstage = d / KC;
+
+  auto load_stage = [&](int s) {
+    const int k0 = s * KC;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int q = tid + i * 256;
+      xr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (q < XCH) {
+        const int tt = q / (KC / V), c = q % (KC / V);
+        if (tt < tt_count)
+          xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * d + k0 + c * V);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int q = tid + i * 256;
+      wreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (q < WCH) {
+        const int e = q / (KC / 4), c = q % (KC / 4);
+        if (e < E) wreg[i] = *reinterpret_cast<const u32x4*>(wr + (size_t)e * d + k0 + c * 4);
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    float* xs = uni + buf * KC * (TT + EP);
+    float* ws = xs + KC * TT;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int q = tid + i * 256;
+      if (q < XCH) {
+        const int tt = q / (KC / V), c = q % (KC / V);
+        float f[V];
+        XLoad<XT>::widen(xr[i], f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) xs[(c * V + v) * TT + tt] = f[v];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int q = tid + i * 256;
+      if (q < WCH) {
+        const int e = q / (KC / 4), c = q % (KC / 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ws[(c * 4 + v) * EP + e] = __uint_as_float(wreg[i][v]);
+      }
+    }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int s = 0; s < nstage; ++s) {
+    if (s + 1 < nstage) load_stage(s + 1);
+    const float* xs = uni + (s & 1) * KC * (TT + EP);
+    const float* ws = xs + KC * TT;
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      float a[MT], b[ME];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) a[i] = xs[kk * TT + tg * MT + i];
+#pragma unroll
+      for (int j = 0; j < ME; ++j) b[j] = ws[kk * EP + eg * ME + j];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < ME; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    if (s + 1 < nstage) store_stage((s + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- logits to LDS: lg[tt * (EP+1) + e]
+  float* lg = uni;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < ME; ++j) lg[(tg * MT + i) * (EP + 1) + eg * ME + j] = acc[i][j];
+  __syncthreads();
+
+  const bool need_z = (p.score == 0) && (p.bias != nullptr || !p.renorm);
+  if (need_z) {
+    // softmax normaliser per token: max, then sum of exp over experts ascending
+    for (int tt = tid; tt < TT; tt += 256) {
+      const float* l = lg + tt * (EP + 1);
+      float m = l[0];
+      for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      float z = 0.0f;
+      for (int e = 0; e < E; ++e) z += canonical_exp(l[e] - m);
+      tok_m[tt] = m;
+      tok_z[tt] = z;
+    }
+    __syncthreads();
+  }
+
+  // ---- top-k: a group of G lanes per token, VPL values per lane
+  {
+    constexpr int G = EP < 64 ? EP : 64;
+    constexpr int VPL = EP / G;
+    constexpr int TPW = 64 / G;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int gi = lane / G, li = lane % G;
+    const bool has_bias = p.bias != nullptr;
+    const bool sigmoid = p.score == 1;
+    for (int base = 0; base < TT; base += 4 * TPW) {
+      const int tt = base + wave * TPW + gi;
+      const float* l = lg + tt * (EP + 1);
+      uint64_t key[VPL];
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        const int e = li + G * q;
+        key[q] = 0ull;
+        if (e < E) {
+          float v = l[e];
+          if (has_bias) {
+            v = sigmoid ? sigmoid_canon(v) + bias_s[e] : canonical_exp(v - tok_m[tt]) / tok_z[tt] + bias_s[e];
+          }
+          key[q] = topk_key(v, e);
+        }
+      }
+      for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int q = 1; q < VPL; ++q) best = key[q] > best ? key[q] : best;
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) {
+          const uint64_t o = __shfl_xor(best, off, G);
+          best = o > best ? o : best;
+        }
+        const int ew = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+          if (li + G * q == ew) key[q] = 0ull;
+        if (li == 0 && tt < tt_count) sel[tt * k + j] = ew;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- combine weights, one thread per token, slots in order
+  for (int tt = tid; tt < tt_count; tt += 256) {
+    const float* l = lg + tt * (EP + 1);
+    const int* s = sel + tt * k;
+    const int64_t t = t0 + tt;
+    if (p.score == 0) {
+      if (p.renorm) {
+        float mk = l[s[0]];
+        for (int j = 1; j < k; ++j) mk = l[s[j]] > mk ? l[s[j]] : mk;
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum += canonical_exp(l[s[j]] - mk);
+        for (int j = 0; j < k; ++j) {
+          p.idx[t * k + j] = s[j];
+          p.w[t * k + j] = canonical_exp(l[s[j]] - mk) / sum;
+        }
+      } else {
+        for (int j = 0; j < k; ++j) {
+          p.idx[t * k + j] = s[j];
+          p.w[t * k + j] = canonical_exp(l[s[j]] - tok_m[tt]) / tok_z[tt];
+        }
+      }
+    } else {
+      float sum = 0.0f;
+      if (p.renorm)
+        for (int j = 0; j < k; ++j) sum += sigmoid_canon(l[s[j]]);
+      for (int j = 0; j < k; ++j) {
+        const float sj = sigmoid_canon(l[s[j]]);
+        p.idx[t * k + j] = s[j];
+        p.w[t * k + j] = p.renorm ? sj / (sum + 1e-9f) : sj;
+      }
+    }
+  }
+
+  if (p.hist) {
+    block_hist_rank(sel, tt_count, k, E, W, masks, p.hist + (size_t)blockIdx.x * E,
+                    p.rank ? p.rank + t0 * k : nullptr);
+  }
+}
+
+// Expert histogram and ranks of blocks of 256 tokens, from expert ids.
+constexpr int kHistTT = 256;
+__global__ __launch_bounds__(256) void k_hist_rank(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                   int32_t* __restrict__ hist, int32_t* __restrict__ rank) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  constexpr int W = kHistTT / 64;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds_raw);
+  int* sel = reinterpret_cast<int*>(masks + (size_t)E * W);
+  const int64_t t0 = (int64_t)blockIdx.x * kHistTT;
+  const int tt_count = (int)((T - t0) < kHistTT ? (T - t0) : kHistTT);
+  for (int q = threadIdx.x; q < E * W; q += 256) masks[q] = 0ull;
+  for (int q = threadIdx.x; q < tt_count * k; q += 256) sel[q] = idx[t0 * k + q];
+  __syncthreads();
+  block_hist_rank(sel, tt_count, k, E, W, masks, hist + (size_t)blockIdx.x * E, rank + t0 * k);
+}
+
+template <int EP>
+hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
+  using S = RouteShape<EP>;
+  const size_t lds = RouteLds<EP>::bytes(a.k);
+  const int64_t nb = (a.T + S::TT - 1) / S::TT;
+  if (a.d % S::KC) return hipErrorInvalidValue;
+  if (a.dtype == 1) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_route<EP, uint16_t>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_route<EP, uint16_t>), dim3((unsigned)nb), dim3(256), lds, s, a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)k_route<EP, float>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_route<EP, float>), dim3((unsigned)nb), dim3(256), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+int padded_experts(int E) {
+  int ep = 8;
+  while (ep < E) ep *= 2;
+  return ep;
+}
+
+}  // namespace
+
+int route_tokens_per_block(int E) {
+  switch (padded_experts(E)) {
+    case 8: return RouteShape<8>::TT;
+    case 16: return RouteShape<16>::TT;
+    case 32: return RouteShape<32>::TT;
+    case 64: return RouteShape<64>::TT;
+    case 128: return RouteShape<128>::TT;
+    case 256: return RouteShape<256>::TT;
+    case 512: return RouteShape<512>::TT;
+    default: return RouteShape<1024>::TT;
+  }
+}
+
+size_t route_lds_bytes(int E, int k) {
+  switch (padded_experts(E)) {
+    case 8: return RouteLds<8>::bytes(k);
+    case 16: return RouteLds<16>::bytes(k);
+    case 32: return RouteLds<32>::bytes(k);
+    case 64: return RouteLds<64>::bytes(k);
+    case 128: return RouteLds<128>::bytes(k);
+    case 256: return RouteLds<256>::bytes(k);
+    case 512: return RouteLds<512>::bytes(k);
+    default: return RouteLds<1024>::bytes(k);
+  }
+}
+
+hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  switch (padded_experts(a.E)) {
+    case 8: return launch_route_ep<8>(a, s);
+    case 16: return launch_route_ep<16>(a, s);
+    case 32: return launch_route_ep<32>(a, s);
+    case 64: return launch_route_ep<64>(a, s);
+    case 128: return launch_route_ep<128>(a, s);
+    case 256: return launch_route_ep<256>(a, s);
+    case 512: return launch_route_ep<512>(a, s);
+    case 1024: return launch_route_ep<1024>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int hist_tokens_per_block() { return kHistTT; }
+
+hipError_t launch_hist_rank(const int32_t* idx, int64_t T, int k, int E, int32_t* hist, int32_t* rank,
+                            hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int64_t nb = (T + kHistTT - 1) / kHistTT;
+  const size_t lds = sizeof(uint64_t) * (size_t)E * (kHistTT / 64) + sizeof(int) * kHistTT * k;
+  hipError_t e = hipFuncSetAttribute((const void*)k_hist_rank, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hist_rank, dim3((unsigned)nb), dim3(256), lds, s, idx, T, k, E, hist, rank);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,194 @@
+"""Python face of libmoe.so: one MoE FFN layer whose weights live in HBM.
+
+PyTorch supplies device memory and the current HIP stream; every computation
+is a call into the C ABI (include/moe.h), whose kernels do all the work.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import _native as N
+from .inputs import LayerConfig
+
+
+def to_device(a: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor]:
+    """Host array (fp32, or bf16 bit patterns as uint16) -> contiguous device tensor."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device).contiguous()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host array (bf16 comes back as uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return N.MOE_BF16
+    if t.dtype == torch.float32:
+        return N.MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Timing:
+    """Per-phase hipEvent timing of moe_forward_timed."""
+
+    def __init__(self):
+        self.lib = N.load()
+        h = ctypes.c_void_p()
+        N.check(self.lib.moe_timing_create(ctypes.byref(h)), "moe_timing_create")
+        self.h = h
+
+    def read(self) -> Dict[str, float]:
+        ms = (ctypes.c_float * N.MOE_N_PHASES)()
+        N.check(self.lib.moe_timing_read(self.h, ms), "moe_timing_read")
+        return {name: float(ms[i]) for i, name in enumerate(N.PHASES)}
+
+    def close(self):
+        if self.h:
+            self.lib.moe_timing_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class MoELayer:
+    """Weights of one layer on the GPU plus its C description."""
+
+    def __init__(self, cfg: LayerConfig, tensors: Dict[str, Optional[torch.Tensor]]):
+        self.lib = N.load()
+        self.cfg = cfg
+        self.t = tensors
+        c = N.MoeLayerC()
+        c.d_model, c.d_ff, c.n_experts, c.top_k = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k
+        c.score = N.MOE_SIGMOID if cfg.score == "sigmoid" else N.MOE_SOFTMAX
+        c.renorm = int(bool(cfg.renorm))
+        c.dtype = N.MOE_BF16 if cfg.dtype == "bf16" else N.MOE_F32
+        c.d_ff_shared = cfg.d_ff_s
+        for name in ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            tt = tensors.get(name)
+            setattr(c, name, None if tt is None else tt.data_ptr())
+        self.c = c
+        self._ws: Optional[torch.Tensor] = None
+        self.device = tensors["w_router"].device
+
+    @classmethod
+    def from_host(cls, cfg: LayerConfig, inputs: Dict[str, Optional[np.ndarray]], device="cuda") -> "MoELayer":
+        names = ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+        return cls(cfg, {n: to_device(inputs.get(n), device) for n in names})
+
+    # -------------------------------------------------------------- helpers
+    def workspace_bytes(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        N.check(self.lib.moe_workspace_size(ctypes.byref(self.c), T, ctypes.byref(n)), "moe_workspace_size")
+        return n.value
+
+    def workspace(self, T: int) -> torch.Tensor:
+        need = max(1, self.workspace_bytes(T))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = None
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def _check_x(self, x: torch.Tensor) -> int:
+        if x.dim() != 2 or x.shape[1] != self.cfg.d_model or not x.is_contiguous():
+            raise ValueError(f"x must be contiguous [T, {self.cfg.d_model}]")
+        if _dtype_code(x) != self.c.dtype:
+            raise TypeError("x dtype does not match the layer dtype")
+        return x.shape[0]
+
+    # ---------------------------------------------------------- entry points
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, want_routing: bool = True,
+                timing: Optional[Timing] = None) -> Dict[str, torch.Tensor]:
+        T = self._check_x(x)
+        k, E, d = self.cfg.top_k, self.cfg.n_experts, self.cfg.d_model
+        dev = x.device
+        if y is None:
+            y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        out = {"y": y}
+        idx = w = counts = None
+        if want_routing:
+            idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+            w = torch.empty((T, k), dtype=torch.float32, device=dev)
+            counts = torch.empty((E,), dtype=torch.int32, device=dev)
+            out.update(idx=idx, w=w, counts=counts)
+        ws = self.workspace(T)
+        args = (ctypes.byref(self.c), _p(x), T, _p(y), _p(idx), _p(w), _p(counts), _p(ws), ws.numel(), _stream())
+        if timing is None:
+            N.check(self.lib.moe_forward(*args), "moe_forward")
+        else:
+            N.check(self.lib.moe_forward_timed(*args, timing.h), "moe_forward_timed")
+        return out
+
+    def route(self, x: torch.Tensor) -> Dict[str, torch.Tensor]:
+        T = self._check_x(x)
+        k, E = self.cfg.top_k, self.cfg.n_experts
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+        counts = torch.empty((E,), dtype=torch.int32, device=x.device)
+        ws = self.workspace(T)
+        N.check(self.lib.moe_route(ctypes.byref(self.c), _p(x), T, _p(idx), _p(w), _p(counts), _p(ws), ws.numel(),
+                                   _stream()), "moe_route")
+        return {"idx": idx, "w": w, "counts": counts}
+
+    def permute(self, x: torch.Tensor, idx: torch.Tensor, with_rows: bool = True) -> Dict[str, torch.Tensor]:
+        T = self._check_x(x)
+        k, E, d = self.cfg.top_k, self.cfg.n_experts, self.cfg.d_model
+        if idx.shape != (T, k) or idx.dtype != torch.int32 or not idx.is_contiguous():
+            raise ValueError("idx must be contiguous int32 [T, k]")
+        x_perm = torch.empty((T * k, d), dtype=x.dtype, device=x.device) if with_rows else None
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=x.device)
+        row_of = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        ws = self.workspace(T)
+        N.check(self.lib.moe_permute(ctypes.byref(self.c), _p(x), T, _p(idx), _p(x_perm), _p(offsets), _p(row_of),
+                                     _p(ws), ws.numel(), _stream()), "moe_permute")
+        return {"x_perm": x_perm, "offsets": offsets, "row_of": row_of}
+
+    def combine(self, y_perm: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor,
+                y_shared: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = row_of.shape[0]
+        y = torch.empty((T, self.cfg.d_model), dtype=torch.float32, device=y_perm.device)
+        N.check(self.lib.moe_combine(ctypes.byref(self.c), T, _p(y_perm), _p(row_of), _p(w), _p(y_shared), _p(y),
+                                     _stream()), "moe_combine")
+        return y
+
+
+def grouped_swiglu(a: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                   w_down: torch.Tensor) -> torch.Tensor:
+    """SwiGLU experts over row groups: out [rows, d_in] fp32 (moe_grouped_swiglu)."""
+    lib = N.load()
+    dt = _dtype_code(a)
+    rows, d_in = a.shape
+    G, d_ff, _ = w_gate.shape
+    n = ctypes.c_size_t()
+    N.check(lib.moe_grouped_swiglu_workspace_size(dt, G, d_in, d_ff, rows, ctypes.byref(n)),
+            "moe_grouped_swiglu_workspace_size")
+    ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=a.device)
+    out = torch.empty((rows, d_in), dtype=torch.float32, device=a.device)
+    N.check(lib.moe_grouped_swiglu(dt, G, d_in, d_ff, rows, _p(a), _p(offsets), _p(w_gate), _p(w_up), _p(w_down),
+                                   _p(out), _p(ws), ws.numel(), _stream()), "moe_grouped_swiglu")
+    return out

@@ -54,6 +54,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp]
     lib.oracle_experts.restype = i32
     lib.oracle_experts.argtypes = [i32, i32, i32, vp, i64, vp, vp, i32, vp, vp, vp, vp]
+    lib.oracle_experts_abs.restype = i32
+    lib.oracle_experts_abs.argtypes = [i32, i32, i32, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     lib.oracle_combine.restype = i32
     lib.oracle_combine.argtypes = [i32, i32, i32, i32, vp, i64, vp, i32, vp, vp, i32,
                                    vp, vp, vp, vp, vp, vp, vp]
@@ -136,8 +138,9 @@ def dispatch(idx: np.ndarray, n_experts: int, L=None) -> Dict[str, np.ndarray]:
     return {"counts": counts, "offsets": offsets, "row_of": row_of}
 
 
-def experts(x, pair_row, pair_expert, w_gate, w_up, w_down, L=None) -> np.ndarray:
-    """fp64 SwiGLU expert outputs for (row, expert) pairs: [n_pairs, d]."""
+def experts(x, pair_row, pair_expert, w_gate, w_up, w_down, L=None, absolute=False) -> np.ndarray:
+    """fp64 SwiGLU expert outputs for (row, expert) pairs: [n_pairs, d].
+    absolute=True gives the magnitude envelope sum_f |W_down| |h_f| instead."""
     x = _c(x)
     pr = _c(pair_row, np.int64)
     pe = _c(pair_expert, np.int32)
@@ -146,8 +149,8 @@ def experts(x, pair_row, pair_expert, w_gate, w_up, w_down, L=None) -> np.ndarra
         wg, wu, wd = wg[None], wu[None], wd[None]
     E, d_ff, d = wg.shape
     out = np.zeros((pr.size, d), np.float64)
-    rc = (L or lib()).oracle_experts(_dt(x), d, d_ff, _p(x), pr.size, _p(pr), _p(pe), E,
-                                     _p(wg), _p(wu), _p(wd), _p(out))
+    fn = (L or lib()).oracle_experts_abs if absolute else (L or lib()).oracle_experts
+    rc = fn(_dt(x), d, d_ff, _p(x), pr.size, _p(pr), _p(pe), E, _p(wg), _p(wu), _p(wd), _p(out))
     if rc != 0:
         raise ValueError("oracle_experts: expert index out of range")
     return out

@@ -348,9 +348,9 @@ static double silu(double z)
  * visited expert by expert (the "sorted loop"), PAIR_BLOCK rows at a time so
  * that each weight row is read once per block.
  */
-int oracle_experts(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, const int64_t *pair_row,
-                   const int32_t *pair_expert, int E, const void *w_gate, const void *w_up, const void *w_down,
-                   double *out)
+static int experts_impl(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, const int64_t *pair_row,
+                        const int32_t *pair_expert, int E, const void *w_gate, const void *w_up, const void *w_down,
+                        double *out, int absolute)
 {
     int64_t *order, *starts, n_blocks = 0, p;
     int64_t *count;
@@ -419,16 +419,21 @@ int oracle_experts(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, c
                         u[b] += wr2[i] * xi[b];
                     }
                 }
-                for (b = 0; b < PAIR_BLOCK; b++)
-                    hb[(size_t)f * PAIR_BLOCK + b] = silu(g[b]) * u[b];
+                for (b = 0; b < PAIR_BLOCK; b++) {
+                    double h = silu(g[b]) * u[b];
+                    hb[(size_t)f * PAIR_BLOCK + b] = absolute ? fabs(h) : h;
+                }
             }
             /* down projection */
             for (c = 0; c < d; c++) {
                 double o[PAIR_BLOCK];
                 for (b = 0; b < PAIR_BLOCK; b++)
                     o[b] = 0.0;
-                for (f = 0; f < d_ff; f++)
+                for (f = 0; f < d_ff; f++) {
                     wr[f] = (double)elem(w_down, dtype, wd_off + (size_t)c * d_ff + f);
+                    if (absolute)
+                        wr[f] = fabs(wr[f]);
+                }
                 for (f = 0; f < d_ff; f++) {
                     const double *hf = hb + (size_t)f * PAIR_BLOCK;
                     for (b = 0; b < PAIR_BLOCK; b++)
@@ -447,6 +452,26 @@ int oracle_experts(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, c
     free(order);
     free(count);
     return 0;
+}
+
+int oracle_experts(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, const int64_t *pair_row,
+                   const int32_t *pair_expert, int E, const void *w_gate, const void *w_up, const void *w_down,
+                   double *out)
+{
+    return experts_impl(dtype, d, d_ff, x, n_pairs, pair_row, pair_expert, E, w_gate, w_up, w_down, out, 0);
+}
+
+/*
+ * Magnitude envelope of the same pairs: sum_f |W_down[e, c, f]| |h_f| with
+ * h = silu(W_gate a) * (W_up a). A relative perturbation of at most u in
+ * every h_f moves the expert output by at most u times this envelope; the
+ * tests use it to bound the effect of storing h in a narrower type.
+ */
+int oracle_experts_abs(int dtype, int d, int d_ff, const void *x, int64_t n_pairs, const int64_t *pair_row,
+                       const int32_t *pair_expert, int E, const void *w_gate, const void *w_up, const void *w_down,
+                       double *out)
+{
+    return experts_impl(dtype, d, d_ff, x, n_pairs, pair_row, pair_expert, E, w_gate, w_up, w_down, out, 1);
 }
 
 /*

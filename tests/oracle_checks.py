@@ -302,5 +302,20 @@ def check_dense_swiglu(L) -> None:
     assert np.array_equal(out2["y"], out["y"][sub])
 
 
+def check_envelope(L) -> None:
+    """The magnitude envelope equals |W_down| |h| computed with numpy fp64."""
+    cfg, inp = small_layer(T=40, d=64, E=3, k=1, d_ff=80)
+    pr = np.arange(40)
+    pe = (np.arange(40) * 7) % 3
+    env = oracle.experts(inp["x"], pr, pe, inp["w_gate"], inp["w_up"], inp["w_down"], L=L, absolute=True)
+    x64 = widen(inp["x"])
+    for i in range(40):
+        e = pe[i]
+        g = widen(inp["w_gate"][e]) @ x64[i]
+        u = widen(inp["w_up"][e]) @ x64[i]
+        ref = np.abs(widen(inp["w_down"][e])) @ np.abs(g / (1.0 + np.exp(-g)) * u)
+        assert np.allclose(env[i], ref, rtol=1e-12, atol=0), f"envelope row {i}"
+
+
 ALL_CHECKS = [check_cexpf, check_logits, check_topk_bruteforce, check_topk_lexsort, check_weights,
-              check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu]
+              check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu, check_envelope]

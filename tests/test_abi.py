@@ -1,0 +1,123 @@
+"""C ABI of libmoe.so on the CPU: the library loads, exports every entry point
+include/moe.h declares, and rejects invalid calls before touching the GPU
+(so no device is needed; pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_02_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return N.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    assert set(names) == set(N.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.moe_status_str(code).decode()
+        assert s.startswith(N.STATUS[code])
+
+
+def layer(**kw):
+    c = N.MoeLayerC()
+    c.d_model, c.d_ff, c.n_experts, c.top_k = 64, 128, 8, 2
+    c.score, c.renorm, c.dtype, c.d_ff_shared = N.MOE_SOFTMAX, 1, N.MOE_BF16, 0
+    c.w_router = c.w_gate = c.w_up = c.w_down = FAKE
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def ws_size(lib, c, T):
+    n = ctypes.c_size_t()
+    st = lib.moe_workspace_size(ctypes.byref(c), T, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 0, 1), ("top_k", 9, 1), ("n_experts", 0, 1), ("d_model", 0, 1),
+    ("d_model", 96, 2), ("d_ff", 100, 2), ("n_experts", 1025, 2), ("dtype", 7, 2), ("score", 3, 2),
+    ("w_router", None, 1), ("w_router", FAKE + 4, 1), ("d_ff_shared", 64, 1), ("ws_gate", FAKE, 1),
+])
+def test_layer_validation(lib, field, value, status):
+    c = layer(**{field: value})
+    assert ws_size(lib, c, 16)[0] == status
+    y = ctypes.c_void_p(FAKE)
+    assert lib.moe_forward(ctypes.byref(c), y, 16, y, None, None, None, y, 1 << 40, None) == status
+
+
+def test_top_k_above_32_unsupported(lib):
+    c = layer(n_experts=64, top_k=33)
+    assert ws_size(lib, c, 16)[0] == 2
+
+
+def test_shared_expert_consistency(lib):
+    ok = layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=128)
+    assert ws_size(lib, ok, 16)[0] == 0
+    assert ws_size(lib, layer(ws_gate=FAKE, ws_up=FAKE, d_ff_shared=128), 16)[0] == 1
+    assert ws_size(lib, layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=0), 16)[0] == 1
+    assert ws_size(lib, layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=96), 16)[0] == 2
+    # the shared expert adds its activations to the workspace
+    assert ws_size(lib, ok, 1000)[1] > ws_size(lib, layer(), 1000)[1]
+
+
+def test_workspace_grows_with_T(lib):
+    c = layer()
+    sizes = [ws_size(lib, c, T)[1] for T in (0, 1, 100, 10000)]
+    assert sizes == sorted(sizes) and sizes[-1] > sizes[1]
+    assert ws_size(lib, c, -1)[0] == 1
+
+
+def test_forward_rejects_before_enqueue(lib):
+    c = layer()
+    p = ctypes.c_void_p(FAKE)
+    st, need = ws_size(lib, c, 100)
+    assert st == 0
+    assert lib.moe_forward(ctypes.byref(c), p, 100, p, None, None, None, p, need - 1, None) == 3
+    assert lib.moe_forward(ctypes.byref(c), p, 100, p, None, None, None, None, need, None) == 3
+    assert lib.moe_forward(ctypes.byref(c), None, 100, p, None, None, None, p, need, None) == 1
+    assert lib.moe_forward(ctypes.byref(c), p, 100, None, None, None, None, p, need, None) == 1
+    assert lib.moe_forward(ctypes.byref(c), ctypes.c_void_p(FAKE + 2), 100, p, None, None, None, p, need, None) == 1
+    assert lib.moe_forward(ctypes.byref(c), p, -5, p, None, None, None, p, need, None) == 1
+    assert lib.moe_forward(None, p, 100, p, None, None, None, p, need, None) == 1
+    c2 = layer(w_gate=None)
+    assert lib.moe_forward(ctypes.byref(c2), p, 100, p, None, None, None, p, need, None) == 1
+
+
+def test_other_entry_points_reject(lib):
+    c = layer()
+    p = ctypes.c_void_p(FAKE)
+    assert lib.moe_route(ctypes.byref(c), None, 10, p, p, None, None, 0, None) == 1
+    assert lib.moe_route(ctypes.byref(c), p, 10, p, p, p, None, 0, None) == 3
+    assert lib.moe_permute(ctypes.byref(c), p, 10, p, p, None, p, p, 1 << 40, None) == 1
+    assert lib.moe_permute(ctypes.byref(c), p, 10, p, p, p, p, None, 0, None) == 3
+    assert lib.moe_combine(ctypes.byref(c), 10, None, p, p, None, p, None) == 1
+    n = ctypes.c_size_t()
+    assert lib.moe_grouped_swiglu_workspace_size(1, 4, 100, 128, 10, ctypes.byref(n)) == 2
+    assert lib.moe_grouped_swiglu_workspace_size(1, 0, 64, 128, 10, ctypes.byref(n)) == 1
+    assert lib.moe_grouped_swiglu_workspace_size(1, 4, 64, 128, 10, ctypes.byref(n)) == 0
+    assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, None, p, p, p, p, p, n.value, None) == 1
+    assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, p, p, p, p, p, p, n.value - 1, None) == 3
+    assert lib.moe_timing_read(None, None) == 1
+    assert lib.moe_forward_timed(ctypes.byref(c), p, 10, p, None, None, None, p, 1 << 40, None, None) == 1

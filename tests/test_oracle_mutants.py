@@ -26,8 +26,7 @@ MUTANTS = {
                               "                s += j ? w[j] : 0.0f;\n            }\n            for (j = 0; j < k; j++)\n"
                               "                w[j] = w[j] / s;"),
     "softmax_bias_on_logits": ("v[e] = oracle_cexpf(l[e] - m) / z + bias[e];", "v[e] = l[e] + bias[e];"),
-    "gate_up_swapped_roles": ("hb[(size_t)f * PAIR_BLOCK + b] = silu(g[b]) * u[b];",
-                              "hb[(size_t)f * PAIR_BLOCK + b] = silu(u[b]) * g[b];"),
+    "gate_up_swapped_roles": ("double h = silu(g[b]) * u[b];", "double h = silu(u[b]) * g[b];"),
     "count_off_by_one": ("        counts[idx[t]]++;\n    if (!logits_out)",
                          "        counts[idx[t] == 0 ? 1 : idx[t]]++;\n    if (!logits_out)"),
 }
