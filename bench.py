@@ -12,7 +12,6 @@ GEMM), and the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,7 +25,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA peaks
 PEAK_VALU_F32_TFLOPS = 78.6                       # fp32 FMA on the VALU without packed instructions
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"gateup": ["mixture_experts_ffn_02_amd/csrc/gemm.hip"]}
+COPY_BYTES = 256 << 20  # plain device-to-device copy used to calibrate HBM counters
 
 
 def parse():
@@ -37,20 +36,16 @@ def parse():
     ap.add_argument("--workload", default="small_sigmoid")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
-
-
-def source_hash(paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch from the committed PMC summary, or None when the
     summary is missing or the kernel source changed since it was taken."""
+    from mixture_experts_ffn_02_amd.profiling import source_hash
+
     path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -60,7 +55,7 @@ def traffic_from_profile(kernel: str, workload: str):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     try:
-        if vals.get("source_sha256") != source_hash(KERNEL_SOURCES[kernel]):
+        if vals.get("source_sha256") != source_hash():
             return None
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -135,6 +130,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     phases = [t.read() for t in timings]
     phase_ms = {k: float(np.mean([p[k] for p in phases])) for k in phases[0]}
     for t in timings:
@@ -144,7 +146,8 @@ def main():
     peak = PEAK_TFLOPS[cfg.dtype]
     gu = work["gateup"]["flops"] / (phase_ms["gateup"] * 1e-3) / 1e12
     traffic = traffic_from_profile("gateup", args.workload)
-    roofline = {"bound": "mfma", "kernel": "k_gemm gate/up (routed)", "achieved": round(gu, 2), "peak": peak,
+    roofline = {"bound": "mfma", "kernel": "k_gemm<bf16, gate/up, grouped> (routed experts)",
+                "achieved": round(gu, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
     detail = {}
     for name, w in work.items():

@@ -6,64 +6,104 @@
 // grouped by expert so that the work scales with routed tokens, not with the
 // number of experts (same section). Two kernels of one template:
 //   gate/up : H[r, n] = silu(sum_k A[r,k] Wg[e,n,k]) * (sum_k A[r,k] Wu[e,n,k]),
-//             stored in the operand dtype (bf16 rounding to nearest even);
+//             stored in the operand dtype (bf16: rounded to nearest even);
 //   down    : Y[r, n] = sum_k H[r,k] Wd[e,n,k], stored in fp32.
-// Both operands are K-contiguous ([rows, K] and [N, K]), which is the layout
-// the MFMA operands want: every lane reads 16 contiguous bytes of one row.
+// Both operands are K-contiguous ([rows, K] and [N, K]): every MFMA lane reads
+// 16 contiguous bytes of one row.
 //
-// Tiling: a block of 256 threads (4 waves, 2 x 2) computes BM = 128 rows x BN
-// output columns (gate/up: 64 columns of H, i.e. 64 gate + 64 up weight rows;
-// down: 128 columns). K advances in stages of 128 bytes per row (64 bf16 or
-// 32 fp32), double-buffered in LDS; global loads of stage s+1 are in flight
-// while stage s feeds the MFMAs. LDS rows are 128 bytes with the 16-byte
-// chunks XOR-swizzled by (row & 7) so that the 16 lanes reading one MFMA
-// fragment column hit distinct banks.
-// MFMA: bf16 v_mfma_f32_16x16x32_bf16 (one per 32-wide K step), fp32
-// v_mfma_f32_16x16x4_f32 (four per 16-wide K step); accumulation in fp32.
-// Row tiles come from a device-side tile list (group, m-tile) written by the
-// dispatch, so no group size ever travels to the host; blocks beyond the
-// list's length exit at once.
+// Work decomposition
+//   * A block of 256 threads (4 waves as 2 x 2) owns an output tile of BM rows
+//     x BN columns; for gate/up the staged weight tile holds BN gate rows and
+//     BN up rows, and each wave keeps gate and up accumulators of the same
+//     (row, column) so the SwiGLU epilogue needs no exchange.
+//   * K advances in stages of SB bytes per row (64 or 128). A stage is copied
+//     from global memory straight into LDS (global_load_lds_dwordx4: lane i
+//     of a wave writes bytes 16i..16i+15 of a 1 KB run); NBUF stage buffers
+//     rotate, so a stage is requested NBUF-1 stages before it is needed.
+//   * The 16-byte chunks of an LDS row are XOR-swizzled so that the 8 lanes
+//     of one ds_read_b128 phase (8 consecutive rows, same logical chunk) hit
+//     8 distinct bank groups. The swizzle is applied on the global side (each
+//     lane fetches the chunk that belongs at its LDS position).
+//   * The grid is persistent: one or two blocks per CU loop over output tiles.
+//     Tiles are split into 8 contiguous ranges, one per XCD (blocks are
+//     dispatched to XCDs round-robin, so block b runs on XCD b % 8), and each
+//     range is walked in groups of GM row tiles x all column tiles, so the
+//     blocks resident on one XCD share weight and activation tiles in that
+//     XCD's L2. Row tiles come from the device-side tile list that the
+//     dispatch wrote (group, m-tile); no group size travels to the host.
+//   * MFMA 32 x 32 tiles: bf16 v_mfma_f32_32x32x16_bf16, fp32
+//     v_mfma_f32_32x32x2_f32 (four per 16-byte chunk); accumulation in fp32.
+//     A stage is SB/32 MFMA K steps; the fragments of the next K step are
+//     read from LDS while the MFMAs of the current one run, and the one
+//     barrier of a stage sits before its last step.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;
-constexpr int kChunks = kRowBytes / 16;
+constexpr int kXcd = 8;
 
-template <typename DT, bool GATEUP, int BN_>
-struct GemmShape {
-  static constexpr int BM = 128;
-  static constexpr int BN = BN_;
-  static constexpr int NB = GATEUP ? 2 * BN : BN;  // weight rows staged per block
-  static constexpr int WN = 2;                     // waves along N (2 along M)
-  static constexpr int TM = BM / 2;
-  static constexpr int TN = BN / WN;
-  static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int NG = GATEUP ? 2 : 1;        // accumulator sets (gate, up)
-  static constexpr int KE = kRowBytes / (int)sizeof(DT);
-  static constexpr int A_CH = BM * kChunks / 256;
-  static constexpr int B_CH = NB * kChunks / 256;
-  static constexpr int LDS = 2 * (BM + NB) * kRowBytes;
+// Tile configuration. SB: bytes of one row in one LDS stage (64 or 128);
+// NBUF: LDS stage buffers.
+template <typename DT, bool GATEUP, int BM_, int BN_, int SB_, int NBUF_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, SB = SB_, NBUF = NBUF_;
+  static constexpr int NB = GATEUP ? 2 * BN : BN;  // weight rows staged per stage
+  static constexpr int TM = BM / 2, TN = BN / 2;   // per wave
+  static constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
+  static constexpr int NG = GATEUP ? 2 : 1;
+  static constexpr int KE = SB / (int)sizeof(DT);  // K elements per stage
+  static constexpr int SPS = SB / 32;              // MFMA K steps (32 bytes each) per stage
+  static constexpr int CPR = SB / 16;              // 16-byte chunks per LDS row
+  static constexpr int RPR = 1024 / SB;            // rows per 1 KB DMA run
+  static constexpr int ROWS = BM + NB;
+  static constexpr int STAGE = ROWS * SB;
+  static constexpr int LPS = ROWS / (4 * RPR);     // DMA runs per wave per stage
+  static constexpr int A_LOADS = BM / (4 * RPR);
+  static constexpr int OCC = STAGE * NBUF > 80 * 1024 ? 1 : 2;  // blocks per CU
+  static_assert(SB == 64 || SB == 128, "stage row bytes");
+  static_assert(BM % (4 * RPR) == 0 && NB % (4 * RPR) == 0 && BN % (4 * RPR) == 0, "DMA runs");
+  static_assert(TN % 32 == 0 && TM % 32 == 0, "tile shape");
+  static_assert(NBUF >= 2 && NBUF <= 5 && STAGE * NBUF <= 160 * 1024, "LDS");
+  static_assert((NBUF - 2) * LPS < 64, "vmcnt range");
+  // XOR key of LDS row `row`: rows of one 128-byte bank window pair up
+  // (SB = 64) so that 8 consecutive rows at one logical chunk hit 8 distinct
+  // bank groups.
+  __device__ static int key(int row) { return (row / (128 / SB)) % CPR; }
+  __device__ static int swz(int row, int chunk) { return row * SB + ((chunk ^ key(row)) << 4); }
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+// s_waitcnt with vmcnt = n (other counters left at their maximum): gfx9
+// encoding, vmcnt split over bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One 32 x 32 MFMA tile over the 16 bytes of K that each lane holds: lane l
+// provides row l % 32 of A (and column l % 32 of B) for K group l / 32.
 template <typename DT>
-__device__ __forceinline__ void mfma_step(f32x4& acc, const u32x4& a, const u32x4& b);
+__device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4& a, const u32x4& b);
 
 template <>
-__device__ __forceinline__ void mfma_step<uint16_t>(f32x4& acc, const u32x4& a, const u32x4& b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+__device__ __forceinline__ void mfma_step<uint16_t>(f32x16& acc, const u32x4& a, const u32x4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
                                                 0, 0, 0);
 }
 
 template <>
-__device__ __forceinline__ void mfma_step<float>(f32x4& acc, const u32x4& a, const u32x4& b) {
+__device__ __forceinline__ void mfma_step<float>(f32x16& acc, const u32x4& a, const u32x4& b) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[q]), __uint_as_float(b[q]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[q]), __uint_as_float(b[q]), acc, 0, 0, 0);
 }
 
 template <typename DT>
@@ -77,176 +117,296 @@ __device__ __forceinline__ float to_out<float>(float v) {
   return v;
 }
 
-template <typename DT, bool GATEUP, int BN>
-__global__ __launch_bounds__(256) void k_gemm(GemmLaunch g) {
-  using S = GemmShape<DT, GATEUP, BN>;
-  __shared__ __align__(16) unsigned char lds[S::LDS];
+__device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned char* lds_run) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+}
+
+// GROUPED: rows come from the tile list over group offsets (routed experts);
+// otherwise one dense group of g.rows rows (the shared expert).
+template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DT, GATEUP, BM, BN, SB, NBUF>::OCC)))
+void k_gemm(GemmLaunch g) {
+  using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
+  __shared__ __align__(16) unsigned char lds[NBUF * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / S::WN, wn = wave % S::WN;
-  const int n_tiles_n = g.N / S::BN;
-  const int64_t tile_m = (int64_t)blockIdx.x / n_tiles_n;
-  const int tile_n = (int)((int64_t)blockIdx.x % n_tiles_n);
-
-  int grp;
-  int64_t row0;
-  int rows;
-  if (g.offsets) {
-    if (tile_m >= g.n_tiles[0]) return;
-    const int2 t = g.tiles[tile_m];
-    if (t.x < 0 || t.x >= g.n_groups || t.y < 0) return;
-    grp = t.x;
-    row0 = (int64_t)g.offsets[grp] + (int64_t)t.y * S::BM;
-    const int64_t left = (int64_t)g.offsets[grp + 1] - row0;
-    rows = (int)(left < S::BM ? left : S::BM);
-  } else {
-    grp = 0;
-    row0 = tile_m * S::BM;
-    const int64_t left = g.rows - row0;
-    rows = (int)(left < S::BM ? left : S::BM);
-  }
-  if (rows <= 0) return;
-  const int n0 = tile_n * S::BN;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_tiles_n = g.N / BN;
+  const int64_t m_tiles = GROUPED ? (int64_t)g.n_tiles[0] : (g.rows + BM - 1) / BM;
+  const int64_t total = m_tiles * n_tiles_n;
+  const int per_xcd = gridDim.x / kXcd;
+  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+  const int64_t chunk = (total + kXcd - 1) / kXcd;
+  const int64_t L0 = xcd * chunk;
+  const int64_t L1 = L0 + chunk < total ? L0 + chunk : total;
   const size_t kbytes = (size_t)g.K * sizeof(DT);
-  const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
-  const unsigned char* B0 = reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
-  const unsigned char* B1 = GATEUP ? reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes : B0;
+  const int nk = g.K / C::KE;
+  const int group_m = g.group_m > 0 ? g.group_m : 8;
+  // Position of this lane in a 1 KB DMA run: row lane / CPR of the run, LDS
+  // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ key(row).
+  const int lrow = lane / C::CPR;
+  const int lchunk = (lane % C::CPR) ^ C::key(lrow);
 
-  // Global sources of this thread's 16-byte chunks and their LDS slots.
-  const unsigned char* a_src[S::A_CH];
-  int a_dst[S::A_CH];
-  bool a_ok[S::A_CH];
-#pragma unroll
-  for (int i = 0; i < S::A_CH; ++i) {
-    const int q = tid + i * 256, r = q >> 3, c = q & 7;
-    a_ok[i] = r < rows;
-    int64_t src_row = row0 + (a_ok[i] ? r : 0);
-    if (g.a_rows) {
-      src_row = g.a_rows[src_row];
-      src_row = src_row < 0 ? 0 : (src_row >= g.a_row_count ? g.a_row_count - 1 : src_row);
+  for (int64_t L = L0 + slot; L < L1; L += per_xcd) {
+    // grouped raster: GM row tiles x every column tile
+    const int64_t gsz = (int64_t)group_m * n_tiles_n;
+    const int64_t first_m = (L / gsz) * group_m;
+    const int64_t gm = (m_tiles - first_m) < group_m ? (m_tiles - first_m) : group_m;
+    const int64_t within = L % gsz;
+    const int64_t tile_m = first_m + within % gm;
+    const int tile_n = (int)(within / gm);
+
+    int grp = 0;
+    int64_t row0;
+    int rows;
+    bool skip = false;
+    if constexpr (GROUPED) {
+      const int2 t = g.tiles[tile_m];
+      skip = t.x < 0 || t.x >= g.n_groups || t.y < 0;
+      grp = skip ? 0 : t.x;
+      row0 = (int64_t)g.offsets[grp] + (int64_t)t.y * BM;
+      const int64_t left = (int64_t)g.offsets[grp + 1] - row0;
+      rows = (int)(left < BM ? left : BM);
+    } else {
+      row0 = tile_m * BM;
+      const int64_t left = g.rows - row0;
+      rows = (int)(left < BM ? left : BM);
     }
-    a_src[i] = A + (size_t)src_row * kbytes + c * 16;
-    a_dst[i] = swz(r, c);
-  }
-  const unsigned char* b_src[S::B_CH];
-  int b_dst[S::B_CH];
-#pragma unroll
-  for (int i = 0; i < S::B_CH; ++i) {
-    const int q = tid + i * 256, r = q >> 3, c = q & 7;
-    const unsigned char* base = (GATEUP && r >= S::BN) ? B1 + (size_t)(n0 + r - S::BN) * kbytes
-                                                       : B0 + (size_t)(n0 + r) * kbytes;
-    b_src[i] = base + c * 16;
-    b_dst[i] = swz(S::BM + r, c);
-  }
+    if (skip || rows <= 0) continue;  // uniform across the block
+    const int n0 = tile_n * BN;
+    const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
+    const unsigned char* B0 = reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
+    const unsigned char* B1 = GATEUP ? reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes : B0;
 
-  u32x4 ra[S::A_CH], rb[S::B_CH];
-  auto gload = [&](int kt) {
-    const size_t off = (size_t)kt * kRowBytes;
+    // Source row of each A run of this lane. Rows past the tile's end read a
+    // valid row; their results are never stored. Weight rows are addressed
+    // from one block-uniform base plus a per-lane offset.
+    int32_t a_row[C::A_LOADS];
 #pragma unroll
-    for (int i = 0; i < S::A_CH; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const u32x4*>(a_src[i] + off) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < S::B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + off);
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* base = lds + buf * (S::BM + S::NB) * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < S::A_CH; ++i) *reinterpret_cast<u32x4*>(base + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < S::B_CH; ++i) *reinterpret_cast<u32x4*>(base + b_dst[i]) = rb[i];
-  };
-
-  f32x4 acc[S::NG][S::FM][S::FN];
-#pragma unroll
-  for (int h = 0; h < S::NG; ++h)
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < S::FN; ++j) acc[h][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = g.K / S::KE;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    const unsigned char* base = lds + (kt & 1) * (S::BM + S::NB) * kRowBytes;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int ch = s * 4 + (lane >> 4);
-      u32x4 af[S::FM];
-#pragma unroll
-      for (int i = 0; i < S::FM; ++i) {
-        const int r = wm * S::TM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const u32x4*>(base + swz(r, ch));
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      int r = (i * 4 + wave) * C::RPR + lrow;
+      r = r < rows ? r : rows - 1;
+      int64_t src_row = row0 + r;
+      if (g.a_rows) {
+        src_row = g.a_rows[src_row];
+        src_row = src_row < 0 ? 0 : (src_row >= g.a_row_count ? g.a_row_count - 1 : src_row);
       }
-#pragma unroll
-      for (int h = 0; h < S::NG; ++h) {
-        u32x4 bfr[S::FN];
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j) {
-          const int r = S::BM + h * S::BN + wn * S::TN + j * 16 + (lane & 15);
-          bfr[j] = *reinterpret_cast<const u32x4*>(base + swz(r, ch));
-        }
-#pragma unroll
-        for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < S::FN; ++j) mfma_step<DT>(acc[h][i][j], af[i], bfr[j]);
-      }
+      a_row[i] = (int32_t)src_row;
     }
-    if (kt + 1 < nk) lstore((kt + 1) & 1);
+    const unsigned char* bbase0 = B0 + (size_t)n0 * kbytes;
+    const unsigned char* bbase1 = B1 + (size_t)n0 * kbytes;
+    const uint32_t lane_off = (uint32_t)((wave * C::RPR + lrow) * kbytes) + lchunk * 16;
+    auto issue = [&](int kt) {
+      unsigned char* sb = lds + (kt % NBUF) * C::STAGE + wave * C::RPR * SB;
+      const size_t off = (size_t)kt * SB;
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i)
+        lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + off + lchunk * 16, sb + i * 4 * C::RPR * SB);
+#pragma unroll
+      for (int i = C::A_LOADS; i < C::LPS; ++i) {
+        const int rb0 = (i - C::A_LOADS) * 4 * C::RPR;
+        const unsigned char* src = (GATEUP && rb0 >= BN) ? bbase1 + (size_t)(rb0 - BN) * kbytes
+                                                         : bbase0 + (size_t)rb0 * kbytes;
+        lds_dma16(src + lane_off + off, sb + i * 4 * C::RPR * SB);
+      }
+    };
+
+    f32x16 acc[C::NG][C::FM][C::FN];
+#pragma unroll
+    for (int h = 0; h < C::NG; ++h)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[h][i][j][e] = 0.0f;
+
+    // Fragments of one K step (s = 0 or 1 of a stage): FM A tiles and
+    // NG x FN weight tiles; lane l reads row l % 32, logical chunk 2s + l/32.
+    struct Frag {
+      u32x4 a[C::FM];
+      u32x4 b[C::NG][C::FN];
+    };
+    auto load_frag = [&](Frag& f, int kt, int s) {
+      const unsigned char* base = lds + (kt % NBUF) * C::STAGE;
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+        f.a[i] = *reinterpret_cast<const u32x4*>(base + C::swz(wm * C::TM + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int h = 0; h < C::NG; ++h)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          f.b[h][j] =
+              *reinterpret_cast<const u32x4*>(base + C::swz(BM + h * BN + wn * C::TN + j * 32 + (lane & 31), ch));
+    };
+    auto mma = [&](const Frag& f) {
+#pragma unroll
+      for (int h = 0; h < C::NG; ++h)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) mfma_step<DT>(acc[h][i][j], f.a[i], f.b[h][j]);
+    };
+    // Wait until stage kt+1 has landed while `ahead` later stages stay in
+    // flight, and until this wave's fragment reads are done.
+    auto wait_stage = [&](int ahead) {
+      if (ahead >= 3 && NBUF >= 5)
+        wait_vm_lgkm0<(NBUF >= 5 ? 3 : 0) * C::LPS>();
+      else if (ahead >= 2 && NBUF >= 4)
+        wait_vm_lgkm0<(NBUF >= 4 ? 2 : 0) * C::LPS>();
+      else if (ahead >= 1 && NBUF >= 3)
+        wait_vm_lgkm0<(NBUF >= 3 ? 1 : 0) * C::LPS>();
+      else
+        wait_vm_lgkm0<0>();
+    };
+
+    // Pipeline: NBUF LDS stages, two fragment sets P and Q alternating over
+    // the SPS K steps of a stage (SPS is even, so step 0 always uses P).
+    // Step s < SPS-1: read step s+1 into the other set, MFMAs of step s.
+    // Last step: wait for stage kt+1 and for this wave's reads, barrier (every
+    // wave is done with stage kt, so its buffer takes stage kt + NBUF), issue
+    // that stage, read step 0 of stage kt+1 into P, MFMAs of the last step.
+    Frag P, Q;
+#pragma unroll
+    for (int q = 0; q < NBUF; ++q)
+      if (q < nk) issue(q);
+    {
+      const int ahead = (nk < NBUF ? nk : NBUF) - 1;  // stages issued after stage 0
+      if (ahead >= 4)
+        wait_vm<(NBUF >= 5 ? 4 : 0) * C::LPS>();
+      else if (ahead == 3)
+        wait_vm<(NBUF >= 4 ? 3 : 0) * C::LPS>();
+      else if (ahead == 2)
+        wait_vm<(NBUF >= 3 ? 2 : 0) * C::LPS>();
+      else if (ahead == 1)
+        wait_vm<C::LPS>();
+      else
+        wait_vm<0>();
+    }
     __syncthreads();
-  }
-
-  // Epilogue. Lane l holds, for each 16 x 16 tile, rows 4*(l/16) + 0..3 of
-  // column l % 16.
+    load_frag(P, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-  for (int i = 0; i < S::FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j) {
-      const int n = n0 + wn * S::TN + j * 16 + (lane & 15);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = wm * S::TM + i * 16 + (lane >> 4) * 4 + rr;
-        if (m >= rows) continue;
-        const size_t o = (size_t)(row0 + m) * g.N + n;
-        if constexpr (GATEUP) {
-          const float gv = acc[0][i][j][rr], uv = acc[1][i][j][rr];
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
-          reinterpret_cast<DT*>(g.out)[o] = to_out<DT>(hv);
+      for (int s = 0; s < C::SPS; ++s) {
+        Frag& cur = (s & 1) ? Q : P;
+        Frag& nxt = (s & 1) ? P : Q;
+        if (s + 1 < C::SPS) {
+          load_frag(nxt, kt, s + 1);
         } else {
-          reinterpret_cast<float*>(g.out)[o] = acc[0][i][j][rr];
+          // stages in flight beyond kt+1: kt+2 .. min(kt+NBUF-1, nk-1)
+          const int last = (kt + NBUF - 1 < nk - 1) ? kt + NBUF - 1 : nk - 1;
+          wait_stage(last - (kt + 1));
+          __syncthreads();
+          if (kt + NBUF < nk) issue(kt + NBUF);
+          if (kt + 1 < nk) load_frag(nxt, kt + 1, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next tile
+
+    // Epilogue. Element e of a 32 x 32 accumulator tile sits in row
+    // 8*(e/4) + 4*(l/32) + e%4 and column l % 32 of lane l. One tile at a
+    // time (scheduling barriers keep the tiles from being interleaved, which
+    // would need more registers than the accumulators leave free).
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int n = n0 + wn * C::TN + j * 32 + (lane & 31);
+        const int mb = wm * C::TM + i * 32 + 4 * (lane >> 5);
+        if constexpr (GATEUP) {
+          DT* out = reinterpret_cast<DT*>(g.out);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = mb + 8 * (e >> 2) + (e & 3);
+            const float gv = acc[0][i][j][e], uv = acc[1][i][j][e];
+            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            if (m < rows) out[(size_t)(row0 + m) * g.N + n] = to_out<DT>(hv);
+          }
+        } else {
+          float* out = reinterpret_cast<float*>(g.out);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = mb + 8 * (e >> 2) + (e & 3);
+            if (m < rows) out[(size_t)(row0 + m) * g.N + n] = acc[0][i][j][e];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 }
 
-template <typename DT, bool GATEUP, int BN>
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
-  using S = GemmShape<DT, GATEUP, BN>;
-  if (g.N % S::BN || g.K % S::KE) return hipErrorInvalidValue;
-  const int64_t m_tiles = g.offsets ? g.max_m_tiles : (g.rows + S::BM - 1) / S::BM;
-  const int64_t blocks = m_tiles * (g.N / S::BN);
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm<DT, GATEUP, BN>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+  using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
+  if (g.N % BN || g.K % C::KE) return hipErrorInvalidValue;
+  int64_t blocks = (int64_t)cu_count() * C::OCC;
+  blocks = (blocks + kXcd - 1) / kXcd * kXcd;
+  if (!g.offsets) {
+    // dense: no more blocks than tiles (rounded up to whole XCD groups)
+    const int64_t tiles = (g.rows + BM - 1) / BM * (g.N / BN);
+    if (tiles <= 0) return hipSuccess;
+    const int64_t need = (tiles + kXcd - 1) / kXcd * kXcd;
+    blocks = need < blocks ? need : blocks;
+  }
+  if (g.offsets)
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, true, BM, BN, SB, NBUF>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, false, BM, BN, SB, NBUF>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_bm(int, bool) { return 128; }
+// Row tile of a grouped GEMM: 256 rows when groups are long enough to fill
+// such tiles and there are enough of them to give every CU several (the
+// persistent grid has one 256-row block per CU), else 128 (less padding in
+// short groups, four times as many tiles).
+int gemm_bm(int dtype, int64_t rows, int64_t groups, int n) {
+  if (dtype != 1 || groups <= 0) return 128;
+  const int64_t avg = rows / groups;
+  const int64_t tiles256 = (rows / 256) * (n / 128);
+  return (avg >= 768 && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
+}
 
-// gate/up: 64 columns of H per block; down: 128 output columns, or 64 when
-// the width is an odd multiple of 64.
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
-  const bool wide = g.N % 128 == 0;
+// gate/up: BN columns of H (gate and up rows staged together); down: BN output
+// columns. The widest tile that divides N.
+hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
   if (g.dtype == 1) {
-    if (g.gateup) return launch_t<uint16_t, true, 64>(g, s);
-    return wide ? launch_t<uint16_t, false, 128>(g, s) : launch_t<uint16_t, false, 64>(g, s);
+    if (g.gateup) {
+      if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2>(g, s);
+      if (bm == 256) return launch_t<uint16_t, true, 256, 64, 128, 2>(g, s);
+      return launch_t<uint16_t, true, 128, 64, 128, 2>(g, s);
+    }
+    if (bm == 256) {
+      if (g.N % 256 == 0) return launch_t<uint16_t, false, 256, 256, 128, 2>(g, s);
+      if (g.N % 128 == 0) return launch_t<uint16_t, false, 256, 128, 128, 2>(g, s);
+      return launch_t<uint16_t, false, 256, 64, 128, 2>(g, s);
+    }
+    if (g.N % 128 == 0) return launch_t<uint16_t, false, 128, 128, 128, 2>(g, s);
+    return launch_t<uint16_t, false, 128, 64, 128, 2>(g, s);
   }
-  if (g.gateup) return launch_t<float, true, 64>(g, s);
-  return wide ? launch_t<float, false, 128>(g, s) : launch_t<float, false, 64>(g, s);
+  if (g.gateup) return launch_t<float, true, 128, 64, 128, 2>(g, s);
+  if (g.N % 128 == 0) return launch_t<float, false, 128, 128, 128, 2>(g, s);
+  return launch_t<float, false, 128, 64, 128, 2>(g, s);
 }
 
 }  // namespace moe

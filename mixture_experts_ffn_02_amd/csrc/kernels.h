@@ -60,10 +60,13 @@ struct GemmLaunch {
   const int2* tiles;
   const int32_t* n_tiles;
   int64_t max_m_tiles;     // grid bound on m-tiles
+  int group_m;             // row tiles per raster group (0: default)
   int64_t rows;            // dense mode: number of rows
 };
-int gemm_bm(int dtype, bool gateup);
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+// Row tile (128 or 256) for `rows` rows in `groups` groups and n output
+// columns; the tile list of a grouped launch must be built with the same value.
+int gemm_bm(int dtype, int64_t rows, int64_t groups, int n);
+hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const int32_t* row_of, const float* w,

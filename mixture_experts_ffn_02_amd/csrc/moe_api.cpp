@@ -58,8 +58,7 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   const int64_t tpb_r = route_tokens_per_block((int)E), tpb_h = hist_tokens_per_block();
   const int64_t tpb = tpb_r < tpb_h ? tpb_r : tpb_h;
   o.nb = (T + tpb - 1) / tpb;
-  const int bm = gemm_bm(L->dtype, true);
-  o.max_tiles = (rows + bm - 1) / bm + E;
+  o.max_tiles = (rows + 127) / 128 + E;  // bound for the smallest row tile
   size_t p = 0;
   auto take = [&](size_t bytes) {
     const size_t at = p;
@@ -143,7 +142,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
   int2* tiles = at<int2>(ws, lo.tiles);
   int32_t* row_of = at<int32_t>(ws, lo.row_of);
   int32_t* tok_of_row = at<int32_t>(ws, lo.tok_of_row);
-  const int bm = gemm_bm(L->dtype, true);
+  const int bm = gemm_bm(L->dtype, (int64_t)T * k, E, L->d_ff);
   const int tpb = route_tokens_per_block(E);
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
@@ -172,7 +171,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
   gu.tiles = tiles;
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
-  MOE_TRY(launch_gemm(gu, s));
+  MOE_TRY(launch_gemm(gu, bm, s));
   mark(tm, MOE_PHASE_DOWN, s);
   GemmLaunch dn = gu;
   dn.gateup = false;
@@ -183,9 +182,10 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
   dn.out = at<void>(ws, lo.yperm);
   dn.N = d;
   dn.K = L->d_ff;
-  MOE_TRY(launch_gemm(dn, s));
+  MOE_TRY(launch_gemm(dn, bm, s));
 
   const float* shared_out = nullptr;
+  const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared);
   mark(tm, MOE_PHASE_SHARED_GATEUP, s);
   if (L->d_ff_shared > 0) {
     GemmLaunch sg{};
@@ -198,7 +198,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
     sg.N = L->d_ff_shared;
     sg.K = d;
     sg.rows = T;
-    MOE_TRY(launch_gemm(sg, s));
+    MOE_TRY(launch_gemm(sg, bm_s, s));
   }
   mark(tm, MOE_PHASE_SHARED_DOWN, s);
   if (L->d_ff_shared > 0) {
@@ -211,7 +211,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
     sd.N = d;
     sd.K = L->d_ff_shared;
     sd.rows = T;
-    MOE_TRY(launch_gemm(sd, s));
+    MOE_TRY(launch_gemm(sd, bm_s, s));
     shared_out = at<float>(ws, lo.ys);
   }
   mark(tm, MOE_PHASE_COMBINE, s);
@@ -292,7 +292,7 @@ moe_status moe_permute(const moe_layer* L, const void* x, int64_t T, const int32
   int32_t* rank = at<int32_t>(ws, lo.rank);
   int32_t* base = at<int32_t>(ws, lo.base);
   MOE_TRY(launch_hist_rank(topk_idx, T, k, E, hist, rank, s));
-  MOE_TRY(launch_scan(hist, (int)nb, E, at<int32_t>(ws, lo.counts), offsets, base, gemm_bm(L->dtype, true),
+  MOE_TRY(launch_scan(hist, (int)nb, E, at<int32_t>(ws, lo.counts), offsets, base, 128,
                       at<int32_t>(ws, lo.n_tiles), at<int2>(ws, lo.tiles), s));
   MOE_TRY(launch_scatter(topk_idx, rank, base, T, k, E, tpb, row_of, at<int32_t>(ws, lo.tok_of_row), x, x_perm,
                          L->d_model * elem_bytes(L->dtype), s));
@@ -305,8 +305,7 @@ moe_status moe_grouped_swiglu_workspace_size(int32_t dtype, int32_t n_groups, in
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d_in % 64 || d_ff % 64) return MOE_ERR_UNSUPPORTED;
   if (rows > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
-  const int bm = gemm_bm(dtype, true);
-  const int64_t max_tiles = (rows + bm - 1) / bm + n_groups;
+  const int64_t max_tiles = (rows + 127) / 128 + n_groups;
   size_t p = align_up(sizeof(int32_t));
   p += align_up(sizeof(int2) * (size_t)max_tiles);
   p += align_up((size_t)elem_bytes(dtype) * (size_t)rows * (size_t)d_ff);
@@ -327,8 +326,8 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const int bm = gemm_bm(dtype, true);
-  const int64_t max_tiles = (rows + bm - 1) / bm + n_groups;
+  const int bm = gemm_bm(dtype, rows, n_groups, d_ff);
+  const int64_t max_tiles = (rows + 127) / 128 + n_groups;
   int32_t* n_tiles = at<int32_t>(ws, 0);
   int2* tiles = at<int2>(ws, align_up(sizeof(int32_t)));
   void* h = at<void>(ws, align_up(sizeof(int32_t)) + align_up(sizeof(int2) * (size_t)max_tiles));
@@ -347,7 +346,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = max_tiles;
   gu.n_groups = n_groups;
-  MOE_TRY(launch_gemm(gu, s));
+  MOE_TRY(launch_gemm(gu, bm, s));
   GemmLaunch dn = gu;
   dn.gateup = false;
   dn.a = h;
@@ -356,7 +355,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   dn.out = out;
   dn.N = d_in;
   dn.K = d_ff;
-  MOE_TRY(launch_gemm(dn, s));
+  MOE_TRY(launch_gemm(dn, bm, s));
   return MOE_OK;
 }
 
