@@ -69,12 +69,15 @@ struct RouteShape;
     static constexpr int EG = EP_ / ME_, TG = 256 / (EP_ / ME_); \
     static constexpr int TT = (256 / (EP_ / ME_)) * MT_;       \
   };
-ROUTE_SHAPE(8, 4, 2, 32)
-ROUTE_SHAPE(16, 4, 4, 32)
-ROUTE_SHAPE(32, 4, 8, 32)
-ROUTE_SHAPE(64, 8, 4, 32)
-ROUTE_SHAPE(128, 8, 8, 32)
-ROUTE_SHAPE(256, 8, 8, 32)
+// Few tokens per block (16-128) so that even the smaller layers spread over
+// every CU; at 256 experts the stage is 16 features so that two blocks fit
+// in one CU's LDS.
+ROUTE_SHAPE(8, 4, 1, 32)
+ROUTE_SHAPE(16, 4, 1, 32)
+ROUTE_SHAPE(32, 4, 2, 32)
+ROUTE_SHAPE(64, 8, 2, 32)
+ROUTE_SHAPE(128, 8, 4, 32)
+ROUTE_SHAPE(256, 8, 8, 16)
 ROUTE_SHAPE(512, 16, 4, 16)
 ROUTE_SHAPE(1024, 16, 4, 8)
 #undef ROUTE_SHAPE
