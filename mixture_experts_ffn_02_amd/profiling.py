@@ -96,6 +96,17 @@ def traffic(args) -> None:
     print(f"fetch_scale: {sf:.4f}")
     print(f"write_scale: {sw:.4f}")
     print(f"hbm_bytes_per_launch: {total:.0f}")
+    if args.rdreq:
+        rq = _counter(args.rdreq, "TCC_EA0_RDREQ_128B_sum")
+        r6 = _counter(args.rdreq, "TCC_EA0_RDREQ_64B_sum")
+        k128, _ = pick(rq, args.kernel)
+        k64, _ = pick(r6, args.kernel)
+        c128, _ = pick(rq, args.copy_kernel)
+        c64, _ = pick(r6, args.copy_kernel)
+        print(f"# cross-check: EA read requests by size (128 B and 64 B); command: "
+              f"{args.cmd.replace('COUNTER', 'TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum')}")
+        print(f"rdreq_bytes_per_dispatch: {128 * k128 + 64 * k64:.0f}")
+        print(f"copy_rdreq_bytes: {128 * c128 + 64 * c64:.0f}")
     print(f"source_sha256: {source_hash()}")
 
 
@@ -109,8 +120,9 @@ def main(argv=None) -> None:
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
     b.add_argument("--kernel", required=True)
-    b.add_argument("--copy-kernel", default="copyBuffer")
+    b.add_argument("--copy-kernel", default="vectorized_elementwise_kernel")
     b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--rdreq", default=None, help="optional run with TCC_EA0_RDREQ_{128B,64B}_sum")
     b.add_argument("--cmd", required=True)
     args = ap.parse_args(argv)
     {"stats": stats, "traffic": traffic}[args.what](args)
