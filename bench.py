@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="small_sigmoid")
+    ap.add_argument("--tokens", type=int, default=0, help="override the workload's token count (small-T sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -115,6 +116,8 @@ def main():
     from mixture_experts_ffn_02_amd.layer import MoELayer, Timing, to_device
 
     cfg = CONFIGS[args.workload]
+    if args.tokens > 0:
+        cfg = cfg.with_tokens(args.tokens)
     inputs = make_layer(cfg)
     layer = MoELayer.from_host(cfg, inputs)
     x = to_device(inputs["x"])
@@ -191,6 +194,14 @@ def main():
             / ((phase_ms["gateup"] + phase_ms["down"] + phase_ms["shared_gateup"] + phase_ms["shared_down"]) * 1e-3)
             / 1e12 / peak, 4),
     }
+    # expert weights the step had to read: experts that received tokens (+ the shared one)
+    counts = layer.route(x)["counts"].cpu().numpy()
+    used = int((counts > 0).sum())
+    wbytes = (2 if cfg.dtype == "bf16" else 4) * 3 * cfg.d_model * (used * cfg.d_ff + cfg.d_ff_s)
+    gemm_ms = phase_ms["gateup"] + phase_ms["down"] + phase_ms["shared_gateup"] + phase_ms["shared_down"]
+    out["expert_weights"] = {"experts_used": used, "bytes": wbytes,
+                             "gbs_over_expert_gemms": round(wbytes / (gemm_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(wbytes / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_seconds)
     print(json.dumps(out), flush=True)

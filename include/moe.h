@@ -111,6 +111,7 @@ moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
  *   topk_idx [T, k] int32 out: expert ids, slot 0 has the largest selection value
  *   topk_w   [T, k] fp32 out: combine weights
  *   counts   [E] int32 out: tokens per expert (may be NULL)
+ *   ws       workspace of at least moe_workspace_size bytes (required when T > 0)
  * Selection value: the logit when sel_bias is NULL; otherwise the score plus
  * the bias (sigmoid: 1/(1+exp(-l)); softmax: exp(l-m)/sum exp(l-m), summed in
  * expert order). Weights: softmax renorm exp(l_j - M)/sum_i exp(l_i - M) over

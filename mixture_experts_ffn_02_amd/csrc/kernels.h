@@ -18,6 +18,7 @@ struct RouteLaunch {
   float* w;               // [T, k]
   int32_t* hist;          // [n_blocks, E] or null
   int32_t* rank;          // [T, k] or null (needs hist)
+  float* logits;          // [T, E] scratch for the small-batch split path, or null (always fused)
 };
 int route_tokens_per_block(int E);
 size_t route_lds_bytes(int E, int k);

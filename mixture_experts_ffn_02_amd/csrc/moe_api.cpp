@@ -44,7 +44,7 @@ moe_status check_layer(const moe_layer* L, bool need_experts) {
 }
 
 struct Layout {
-  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, h, yperm, hs, ys, total;
+  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, logits, h, yperm, hs, ys, total;
   int64_t nb;         // histogram rows (blocks)
   int64_t max_tiles;  // bound on grouped GEMM row tiles
 };
@@ -76,6 +76,7 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   o.tok_of_row = take(sizeof(int32_t) * (size_t)rows);
   o.idx = take(sizeof(int32_t) * (size_t)rows);
   o.w = take(sizeof(float) * (size_t)rows);
+  o.logits = take(sizeof(float) * (size_t)(T * E));
   o.h = take((size_t)eb * (size_t)(rows * f));
   o.yperm = take(sizeof(float) * (size_t)(rows * d));
   o.hs = take((size_t)eb * (size_t)(T * fs));
@@ -147,7 +148,8 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
   mark(tm, MOE_PHASE_ROUTE, s);
-  RouteLaunch r{x, L->dtype, T, d, E, k, L->score, L->renorm, L->w_router, L->sel_bias, idx_p, w_p, hist, rank};
+  RouteLaunch r{x, L->dtype, T, d, E, k, L->score, L->renorm, L->w_router, L->sel_bias, idx_p, w_p, hist, rank,
+                at<float>(ws, lo.logits)};
   MOE_TRY(launch_route(r, s));
   mark(tm, MOE_PHASE_SCAN, s);
   MOE_TRY(launch_scan(hist, (int)nb_route, E, counts_p, offsets, base, bm, n_tiles, tiles, s));
@@ -251,7 +253,7 @@ moe_status moe_route(const moe_layer* L, const void* x, int64_t T, int32_t* topk
   if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
   if (T > 0 && (!x || !topk_idx || !topk_w || !aligned16(x))) return MOE_ERR_INVALID;
   const Layout lo = make_layout(L, T);
-  if (T > 0 && counts && (!ws || ws_bytes < lo.total)) return MOE_ERR_WORKSPACE;
+  if (T > 0 && (!ws || ws_bytes < lo.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (T == 0) {
@@ -260,7 +262,7 @@ moe_status moe_route(const moe_layer* L, const void* x, int64_t T, int32_t* topk
   }
   int32_t* hist = counts ? at<int32_t>(ws, lo.hist) : nullptr;
   RouteLaunch r{x, L->dtype, T, L->d_model, L->n_experts, L->top_k, L->score, L->renorm, L->w_router,
-                L->sel_bias, topk_idx, topk_w, hist, nullptr};
+                L->sel_bias, topk_idx, topk_w, hist, nullptr, at<float>(ws, lo.logits)};
   MOE_TRY(launch_route(r, s));
   if (counts) {
     const int tpb = route_tokens_per_block(L->n_experts);

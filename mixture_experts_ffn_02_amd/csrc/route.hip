@@ -144,7 +144,9 @@ __device__ void block_hist_rank(const int* sel, int tt_count, int k, int E, int 
   }
 }
 
-template <int EP, typename XT>
+// FROM_LOGITS: the logits were computed by k_logits into p.logits [T, E];
+// otherwise the gate product runs here, fused with the selection.
+template <int EP, typename XT, bool FROM_LOGITS>
 __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   using S = RouteShape<EP>;
   using L = RouteLds<EP>;
@@ -169,6 +171,15 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   for (int e = tid; e < EP; e += 256) bias_s[e] = (p.bias && e < E) ? p.bias[e] : 0.0f;
   for (int q = tid; q < EP * W; q += 256) masks[q] = 0ull;
 
+  float* lg = uni;
+  if constexpr (FROM_LOGITS) {
+    // logits of this block's tokens, rows of E contiguous floats
+    for (int q = tid; q < TT * EP; q += 256) {
+      const int tt = q / EP, e = q % EP;
+      lg[tt * (EP + 1) + e] = (tt < tt_count && e < E) ? p.logits[(t0 + tt) * E + e] : 0.0f;
+    }
+    __syncthreads();
+  } else {
   // ---- gate product: logits[tt][e] = fma chain over features ascending
   const int tg = tid % TG, eg = tid / TG;
   float acc[MT][ME];
@@ -255,12 +266,12 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   }
 
   // ---- logits to LDS: lg[tt * (EP+1) + e]
-  float* lg = uni;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < ME; ++j) lg[(tg * MT + i) * (EP + 1) + eg * ME + j] = acc[i][j];
   __syncthreads();
+  }
 
   const bool need_z = (p.score == 0) && (p.bias != nullptr || !p.renorm);
   if (need_z) {
@@ -360,6 +371,78 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   }
 }
 
+// Gate product alone, for batches too small to fill the GPU with whole-row
+// router blocks: a block owns 16 tokens x 64 experts (thread: 1 token x 4
+// experts), so the grid also spans the experts. Each logit is still one fma
+// chain over features ascending, identical to the fused kernel's.
+constexpr int kLogTT = 16, kLogTE = 64, kLogKC = 32;
+template <typename XT>
+__global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
+  constexpr int V = XLoad<XT>::V;
+  __shared__ __align__(16) float xs[2][kLogKC][kLogTT];
+  __shared__ __align__(16) float ws[2][kLogKC][kLogTE];
+  const int tid = threadIdx.x;
+  const int tg = tid % kLogTT, eg = tid / kLogTT;  // 16 x 16
+  const int64_t t0 = (int64_t)blockIdx.x * kLogTT;
+  const int e0 = blockIdx.y * kLogTE;
+  const int d = p.d, E = p.E;
+  const XT* __restrict__ x = reinterpret_cast<const XT*>(p.x);
+  constexpr int XCH = kLogTT * kLogKC / V;  // 16-byte x loads per stage
+  constexpr int WCH = kLogTE * kLogKC / 4;  // 512
+  u32x4 xr = u32x4{0u, 0u, 0u, 0u}, wreg[WCH / 256];
+  auto load = [&](int st) {
+    const int k0 = st * kLogKC;
+    if (tid < XCH) {
+      const int tt = tid / (kLogKC / V), c = tid % (kLogKC / V);
+      xr = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + tt < p.T) xr = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * d + k0 + c * V);
+    }
+#pragma unroll
+    for (int i = 0; i < WCH / 256; ++i) {
+      const int q = tid + i * 256, e = q / (kLogKC / 4), c = q % (kLogKC / 4);
+      wreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (e0 + e < E) wreg[i] = *reinterpret_cast<const u32x4*>(p.w_router + (size_t)(e0 + e) * d + k0 + c * 4);
+    }
+  };
+  auto store = [&](int buf) {
+    if (tid < XCH) {
+      const int tt = tid / (kLogKC / V), c = tid % (kLogKC / V);
+      float f[V];
+      XLoad<XT>::widen(xr, f);
+#pragma unroll
+      for (int v = 0; v < V; ++v) xs[buf][c * V + v][tt] = f[v];
+    }
+#pragma unroll
+    for (int i = 0; i < WCH / 256; ++i) {
+      const int q = tid + i * 256, e = q / (kLogKC / 4), c = q % (kLogKC / 4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ws[buf][c * 4 + v][e] = __uint_as_float(wreg[i][v]);
+    }
+  };
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int nst = d / kLogKC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) load(st + 1);
+    const int b = st & 1;
+#pragma unroll 8
+    for (int kk = 0; kk < kLogKC; ++kk) {
+      const float a = xs[b][kk][tg];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(a, ws[b][kk][eg * 4 + j], acc[j]);
+    }
+    if (st + 1 < nst) store((st + 1) & 1);
+    __syncthreads();
+  }
+  if (t0 + tg < p.T) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e0 + eg * 4 + j < E) p.logits[(t0 + tg) * E + e0 + eg * 4 + j] = acc[j];
+  }
+}
+
 // Expert histogram and ranks of blocks of 256 tokens, from expert ids.
 constexpr int kHistTT = 256;
 __global__ __launch_bounds__(256) void k_hist_rank(const int32_t* __restrict__ idx, int64_t T, int k, int E,
@@ -376,24 +459,44 @@ __global__ __launch_bounds__(256) void k_hist_rank(const int32_t* __restrict__ i
   block_hist_rank(sel, tt_count, k, E, W, masks, hist + (size_t)blockIdx.x * E, rank + t0 * k);
 }
 
+template <typename K>
+hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLaunch& a) {
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+int cu_count_route() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    n = (hipGetDevice(&dev) == hipSuccess &&
+         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ? v
+            : 256;
+  }
+  return n;
+}
+
 template <int EP>
 hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   using S = RouteShape<EP>;
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
-  if (a.d % S::KC) return hipErrorInvalidValue;
-  if (a.dtype == 1) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_route<EP, uint16_t>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (a.d % S::KC || a.d % kLogKC) return hipErrorInvalidValue;
+  // Split path when whole-row blocks would leave CUs idle and the experts are
+  // many: logits first (grid over tokens and experts), then the selection.
+  const bool split = a.logits != nullptr && a.E >= 64 && 4 * nb < cu_count_route();
+  if (split) {
+    const dim3 g((unsigned)((a.T + kLogTT - 1) / kLogTT), (unsigned)((a.E + kLogTE - 1) / kLogTE));
+    hipError_t e = a.dtype == 1 ? launch_k(k_logits<uint16_t>, g, 0, s, a) : launch_k(k_logits<float>, g, 0, s, a);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_route<EP, uint16_t>), dim3((unsigned)nb), dim3(256), lds, s, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void*)k_route<EP, float>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_route<EP, float>), dim3((unsigned)nb), dim3(256), lds, s, a);
+    return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, true>, dim3((unsigned)nb), lds, s, a)
+                        : launch_k(k_route<EP, float, true>, dim3((unsigned)nb), lds, s, a);
   }
-  return hipGetLastError();
+  return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, false>, dim3((unsigned)nb), lds, s, a)
+                      : launch_k(k_route<EP, float, false>, dim3((unsigned)nb), lds, s, a);
 }
 
 int padded_experts(int E) {
