@@ -50,6 +50,10 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_logits.argtypes = [i32, vp, i64, i32, vp, i32, vp]
     lib.oracle_route.restype = i32
     lib.oracle_route.argtypes = [i32, vp, i64, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.oracle_route_ex.restype = i32
+    lib.oracle_route_ex.argtypes = [i32, vp, i64, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.oracle_router_metrics.argtypes = [vp, vp, i64, i32, i32, i32, vp]
+    lib.oracle_bias_update.argtypes = [vp, i32, ctypes.c_float, vp]
     lib.oracle_dispatch.restype = i32
     lib.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp]
     lib.oracle_experts.restype = i32
@@ -107,22 +111,47 @@ def logits(x: np.ndarray, w_router: np.ndarray, L=None) -> np.ndarray:
     return out
 
 
-def route(x, w_router, sel_bias, top_k, score="softmax", renorm=True, L=None) -> Dict[str, np.ndarray]:
-    """fp32 router: idx [T,k] int32, w [T,k] fp32, counts [E] int32, logits [T,E]."""
+def route(x, w_router, sel_bias, top_k, score="softmax", renorm=True, L=None, bias_on_logits=False,
+          noise=None) -> Dict[str, np.ndarray]:
+    """fp32 router: idx [T,k] int32, w [T,k] fp32, counts [E] int32, logits [T,E].
+    bias_on_logits: the bias enters the logit instead of the score; noise
+    [T,E] fp32 is added to the selection value (training-time exploration)."""
     x = _c(x)
     wr = _c(w_router, np.float32)
     b = _c(sel_bias, np.float32)
+    nz = _c(noise, np.float32)
     T, d = x.shape
     E = wr.shape[0]
     idx = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
     counts = np.empty(E, np.int32)
     lg = np.empty((T, E), np.float32)
-    rc = (L or lib()).oracle_route(_dt(x), _p(x), T, d, _p(wr), _p(b), E, top_k, SCORE[score], int(bool(renorm)),
-                                   _p(idx), _p(w), _p(counts), _p(lg))
+    rc = (L or lib()).oracle_route_ex(_dt(x), _p(x), T, d, _p(wr), _p(b), int(bool(bias_on_logits)), _p(nz), E,
+                                      top_k, SCORE[score], int(bool(renorm)), _p(idx), _p(w), _p(counts), _p(lg))
     if rc != 0:
         raise ValueError("oracle_route: bad arguments")
     return {"idx": idx, "w": w, "counts": counts, "logits": lg}
+
+
+METRICS = ("z_loss", "aux_loss", "cv", "entropy_bits", "load_max_ratio", "unused_frac")
+
+
+def router_metrics(logits, idx, score="softmax", L=None) -> np.ndarray:
+    """fp64 router losses and health metrics, in the order of METRICS."""
+    lg = _c(logits, np.float32)
+    idx = _c(idx, np.int32)
+    T, E = lg.shape
+    out = np.zeros(len(METRICS), np.float64)
+    (L or lib()).oracle_router_metrics(_p(lg), _p(idx), T, E, idx.shape[1], SCORE[score], _p(out))
+    return out
+
+
+def bias_update(counts, bias, rate, L=None) -> np.ndarray:
+    """One step of the aux-loss-free balance controller; returns the new bias."""
+    c = _c(counts, np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    (L or lib()).oracle_bias_update(_p(c), c.size, float(rate), _p(b))
+    return b
 
 
 def dispatch(idx: np.ndarray, n_experts: int, L=None) -> Dict[str, np.ndarray]:

@@ -191,15 +191,15 @@ static float sigmoidf_canon(float l)
  * Routing of one token from its fp32 logits l[0..E-1]: selection values,
  * top-k, combine weights.
  */
-static void route_token(const float *l, const float *bias, int E, int k, int score, int renorm,
-                        float *v, unsigned char *taken, int32_t *idx, float *w)
+static void route_token(const float *l, const float *bias, int bias_on_logits, const float *noise, int E, int k,
+                        int score, int renorm, float *v, unsigned char *taken, int32_t *idx, float *w)
 {
     int e, j;
     float m = 0.0f, z = 0.0f;
 
     /* Softmax normaliser over all experts: only needed for a softmax score
-     * that is biased or not renormalised. */
-    if (score == SCORE_SOFTMAX && (bias || !renorm)) {
+     * that is biased in score space or not renormalised. */
+    if (score == SCORE_SOFTMAX && ((bias && !bias_on_logits) || !renorm)) {
         m = l[0];
         for (e = 1; e < E; e++)
             if (l[e] > m)
@@ -209,14 +209,20 @@ static void route_token(const float *l, const float *bias, int E, int k, int sco
             z += oracle_cexpf(l[e] - m);
     }
 
-    /* selection value */
+    /* selection value; the bias enters the score (default) or the logit
+     * (the README's SigmoidRouter code), exploration noise (training only)
+     * is added last */
     for (e = 0; e < E; e++) {
         if (!bias)
             v[e] = l[e];
+        else if (bias_on_logits)
+            v[e] = l[e] + bias[e];
         else if (score == SCORE_SIGMOID)
             v[e] = sigmoidf_canon(l[e]) + bias[e];
         else
             v[e] = oracle_cexpf(l[e] - m) / z + bias[e];
+        if (noise)
+            v[e] = v[e] + noise[e];
     }
 
     /* top-k: k times, the largest remaining value; on a tie the lower index
@@ -268,8 +274,9 @@ static void route_token(const float *l, const float *bias, int E, int k, int sco
  * w [T, k] fp32, counts [E] (tokens per expert). logits_out [T, E] is
  * optional. Returns 0, or -1 on bad arguments.
  */
-int oracle_route(int dtype, const void *x, int64_t T, int d, const float *w_router, const float *sel_bias,
-                 int E, int k, int score, int renorm, int32_t *idx, float *w, int32_t *counts, float *logits_out)
+int oracle_route_ex(int dtype, const void *x, int64_t T, int d, const float *w_router, const float *sel_bias,
+                    int bias_on_logits, const float *noise, int E, int k, int score, int renorm, int32_t *idx,
+                    float *w, int32_t *counts, float *logits_out)
 {
     float *logits;
     int64_t t;
@@ -284,8 +291,8 @@ int oracle_route(int dtype, const void *x, int64_t T, int d, const float *w_rout
         unsigned char *taken = (unsigned char *)malloc((size_t)E);
 #pragma omp for schedule(static)
         for (t = 0; t < T; t++)
-            route_token(logits + (size_t)t * E, sel_bias, E, k, score, renorm, v, taken, idx + (size_t)t * k,
-                        w + (size_t)t * k);
+            route_token(logits + (size_t)t * E, sel_bias, bias_on_logits, noise ? noise + (size_t)t * E : NULL, E, k,
+                        score, renorm, v, taken, idx + (size_t)t * k, w + (size_t)t * k);
         free(v);
         free(taken);
     }
@@ -296,6 +303,110 @@ int oracle_route(int dtype, const void *x, int64_t T, int d, const float *w_rout
     if (!logits_out)
         free(logits);
     return 0;
+}
+
+int oracle_route(int dtype, const void *x, int64_t T, int d, const float *w_router, const float *sel_bias,
+                 int E, int k, int score, int renorm, int32_t *idx, float *w, int32_t *counts, float *logits_out)
+{
+    return oracle_route_ex(dtype, x, T, d, w_router, sel_bias, 0, NULL, E, k, score, renorm, idx, w, counts,
+                           logits_out);
+}
+
+/*
+ * Router losses and health metrics of one forward pass (README,
+ * "SigmoidRouter": z-loss, aux loss, counts, coefficient of variation,
+ * entropy of the mean score distribution; SpecForge PR #931, "What to
+ * watch": max/mean load and the share of unused experts), in fp64 from the
+ * fp32 logits and the chosen ids:
+ *   out[0] z_loss         mean over tokens of logsumexp(logits)^2
+ *   out[1] aux_loss       E * sum_i f_i P_i, f_i = counts_i / T,
+ *                         P_i = mean over tokens of the score of expert i
+ *   out[2] cv             std(counts, unbiased) / max(mean(counts), 1); 0 for E = 1
+ *   out[3] entropy_bits   -sum p log2 p, p = max(P, 1e-9) normalised to sum 1
+ *   out[4] load_max_ratio max(counts) / mean(counts)
+ *   out[5] unused_frac    share of experts with no token
+ * Scores are sigmoid(logit) or the softmax over all experts.
+ */
+void oracle_router_metrics(const float *logits, const int32_t *idx, int64_t T, int E, int k, int score, double *out)
+{
+    double *P = (double *)calloc((size_t)E, sizeof(double));
+    double *cnt = (double *)calloc((size_t)E, sizeof(double));
+    double z = 0.0, aux = 0.0, mean, var = 0.0, ent = 0.0, psum = 0.0, mx = 0.0;
+    int64_t t;
+    int e, unused = 0;
+    for (t = 0; t < T; t++) {
+        const float *l = logits + (size_t)t * E;
+        double m = l[0], s = 0.0, lse;
+        for (e = 1; e < E; e++)
+            if (l[e] > m)
+                m = l[e];
+        for (e = 0; e < E; e++)
+            s += exp((double)l[e] - m);
+        lse = m + log(s);
+        z += lse * lse;
+        for (e = 0; e < E; e++)
+            P[e] += score == SCORE_SIGMOID ? 1.0 / (1.0 + exp(-(double)l[e])) : exp((double)l[e] - m) / s;
+    }
+    for (t = 0; t < T * k; t++)
+        cnt[idx[t]] += 1.0;
+    mean = (double)(T * k) / E;
+    for (e = 0; e < E; e++) {
+        P[e] /= (double)T;
+        aux += (cnt[e] / (double)T) * P[e];
+        var += (cnt[e] - mean) * (cnt[e] - mean);
+        if (cnt[e] > mx)
+            mx = cnt[e];
+        if (cnt[e] == 0.0)
+            unused++;
+        psum += P[e] > 1e-9 ? P[e] : 1e-9;
+    }
+    for (e = 0; e < E; e++) {
+        double p = (P[e] > 1e-9 ? P[e] : 1e-9) / psum;
+        ent -= p * log(p);
+    }
+    out[0] = T > 0 ? z / (double)T : 0.0;
+    out[1] = (double)E * aux;
+    out[2] = E > 1 ? sqrt(var / (double)(E - 1)) / (mean > 1.0 ? mean : 1.0) : 0.0;
+    out[3] = ent / log(2.0);
+    out[4] = mean > 0.0 ? mx / mean : 0.0;
+    out[5] = (double)unused / E;
+    free(P);
+    free(cnt);
+}
+
+/*
+ * Aux-loss-free balance controller, applied after a forward pass so that the
+ * next forward selects with the new bias (README, "SigmoidRouter",
+ * step_bias_update; SpecForge PR #930 "Tests": deferred balance update).
+ * In fp32, in the order of that code:
+ *   p_i = counts_i / max(sum counts, 1);  err = 1/E - p_i;
+ *   err += 0.5 where p_i < 0.1 / E (starved expert);  bias += err * rate;
+ *   bias = clamp(bias, -10, 10).
+ * The constants 1/E and 0.1/E are formed in fp64 and rounded to fp32 once,
+ * as a Python scalar meets an fp32 tensor; the sum of counts is exact
+ * integer arithmetic.
+ */
+void oracle_bias_update(const int32_t *counts, int E, float rate, float *bias)
+{
+    int64_t sum = 0;
+    float total, target = (float)(1.0 / E), starved = (float)(0.1 * (1.0 / E));
+    int e;
+    for (e = 0; e < E; e++)
+        sum += counts[e];
+    total = (float)sum;
+    if (total < 1.0f)
+        total = 1.0f;
+    for (e = 0; e < E; e++) {
+        float p = (float)counts[e] / total;
+        float err = target - p;
+        if (p < starved)
+            err = err + 0.5f;
+        bias[e] = bias[e] + err * rate;
+        if (bias[e] < -10.0f)
+            bias[e] = -10.0f;
+        if (bias[e] > 10.0f)
+            bias[e] = 10.0f;
+    }
 }
 
 /*

@@ -317,5 +317,151 @@ def check_envelope(L) -> None:
         assert np.allclose(env[i], ref, rtol=1e-12, atol=0), f"envelope row {i}"
 
 
+# ---------------------------------------------------------------------------
+# selection options: bias in logit space, exploration noise
+# ---------------------------------------------------------------------------
+
+def check_route_options(L) -> None:
+    """Bias in logit space (README, "SigmoidRouter": logits + bias select):
+    the chosen set is the brute-force order of fp64 logit + bias wherever the
+    gap is wide, a bias that is the same for every expert changes nothing,
+    and the weights stay the renormalised unbiased scores. Noise: zero noise
+    is no noise, bitwise; a large noise on one expert puts it in slot 0; noise
+    that reproduces a bias (noise[t, e] = b[e]) selects as that bias does."""
+    for score in ("sigmoid", "softmax"):
+        cfg, inp = small_layer(T=256, d=64, E=16, k=4, score=score, bias_range=0.5)
+        x, wr, b = inp["x"], inp["w_router"], inp["sel_bias"]
+        plain = oracle.route(x, wr, None, 4, score, True, L=L)
+        lg = plain["logits"].astype(np.float64)
+        r = oracle.route(x, wr, b, 4, score, True, L=L, bias_on_logits=True)
+        v = lg + b.astype(np.float64)
+        srt = np.sort(v, 1)[:, ::-1]
+        wide = (srt[:, 3] - srt[:, 4]) > 1e-5
+        assert wide.sum() > 200
+        for t in np.nonzero(wide)[0]:
+            order = np.lexsort((np.arange(16), -v[t]))[:4]
+            assert np.array_equal(r["idx"][t], order), f"{score}: logit-space bias, token {t}"
+        moved = np.any(r["idx"] != plain["idx"], 1)
+        assert moved.any(), "a logit-space bias of +-0.5 moved no token"
+        sel = np.take_along_axis(lg, r["idx"], 1)
+        if score == "sigmoid":
+            ss = 1.0 / (1.0 + np.exp(-sel))
+            ref = ss / (ss.sum(1, keepdims=True) + 1e-9)
+        else:
+            ref = np.exp(sel - sel.max(1, keepdims=True))
+            ref /= ref.sum(1, keepdims=True)
+        assert np.allclose(r["w"], ref, rtol=1e-6, atol=0), f"{score}: weights under a logit-space bias"
+        const = np.full(16, 0.25, np.float32)
+        c = oracle.route(x, wr, const, 4, score, True, L=L, bias_on_logits=True)
+        srt0 = np.sort(lg, 1)[:, ::-1]
+        wide0 = (srt0[:, 3] - srt0[:, 4]) > 1e-5
+        assert np.array_equal(c["idx"][wide0], plain["idx"][wide0]), f"{score}: constant logit bias moved tokens"
+        zero = oracle.route(x, wr, b, 4, score, True, L=L, noise=np.zeros((256, 16), np.float32))
+        ref_b = oracle.route(x, wr, b, 4, score, True, L=L)
+        assert np.array_equal(zero["idx"], ref_b["idx"]) and np.array_equal(zero["w"], ref_b["w"])
+        big = np.zeros((256, 16), np.float32)
+        big[np.arange(256), np.arange(256) % 16] = 100.0
+        f = oracle.route(x, wr, b, 4, score, True, L=L, noise=big)
+        assert np.array_equal(f["idx"][:, 0], np.arange(256) % 16), f"{score}: noise did not force slot 0"
+        as_noise = oracle.route(x, wr, None, 4, score, True, L=L, noise=np.tile(b, (256, 1)))
+        as_bias = oracle.route(x, wr, b, 4, score, True, L=L, bias_on_logits=True)
+        assert np.array_equal(as_noise["idx"], as_bias["idx"]) and np.array_equal(as_noise["w"], as_bias["w"])
+
+
+# ---------------------------------------------------------------------------
+# router losses and health metrics
+# ---------------------------------------------------------------------------
+
+def check_router_metrics(L) -> None:
+    """z-loss, aux loss, cv, entropy, max/mean load and unused share
+    (README, "SigmoidRouter"; PR #931, "What to watch") against
+    * closed forms at all-zero logits, where every token takes experts 0..k-1:
+      z = (ln E)^2, aux = k (softmax) or E k / 2 (sigmoid), entropy = log2 E,
+      cv = sqrt(E (E-k) / (k (E-1))), max/mean = E/k, unused = (E-k)/E;
+    * perfectly balanced one-hot routing: cv 0, max/mean 1, unused 0;
+    * scipy's logsumexp and entropy and numpy's unbiased std on a random layer."""
+    from scipy.special import logsumexp
+    from scipy.stats import entropy
+
+    for E, k in ((8, 2), (16, 4), (5, 1)):
+        T = 64
+        lg = np.zeros((T, E), np.float32)
+        idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+        for score, aux in (("softmax", k), ("sigmoid", E * k / 2)):
+            m = oracle.router_metrics(lg, idx, score, L=L)
+            exp = [math.log(E) ** 2, aux, math.sqrt(E * (E - k) / (k * (E - 1))), math.log2(E), E / k, (E - k) / E]
+            assert np.allclose(m, exp, rtol=1e-12, atol=1e-15), f"E={E} k={k} {score}: {m} vs {exp}"
+    # balanced one-hot routing
+    E, T = 8, 64
+    lg = np.full((T, E), -20.0, np.float32)
+    lg[np.arange(T), np.arange(T) % E] = 20.0
+    idx = (np.arange(T) % E).astype(np.int32)[:, None]
+    m = oracle.router_metrics(lg, idx, "softmax", L=L)
+    assert m[2] == 0.0 and m[4] == 1.0 and m[5] == 0.0, m
+    assert abs(m[1] - 1.0) < 1e-12 and abs(m[3] - 3.0) < 1e-12, m
+    # random layer: library routines
+    for score in ("softmax", "sigmoid"):
+        cfg, inp = small_layer(T=300, d=64, E=12, k=3, score=score, bias_range=0.3)
+        r = oracle.route(inp["x"], inp["w_router"], inp["sel_bias"], 3, score, True, L=L)
+        lg = r["logits"].astype(np.float64)
+        m = oracle.router_metrics(r["logits"], r["idx"], score, L=L)
+        lse = logsumexp(lg, axis=1)
+        sc = 1.0 / (1.0 + np.exp(-lg)) if score == "sigmoid" else np.exp(lg - lse[:, None])
+        cnt = np.bincount(r["idx"].ravel(), minlength=12).astype(np.float64)
+        P = sc.mean(0)
+        exp = [np.mean(lse ** 2), 12 * np.sum(cnt / 300 * P), np.std(cnt, ddof=1) / max(cnt.mean(), 1.0),
+               entropy(np.maximum(P, 1e-9), base=2), cnt.max() / cnt.mean(), np.mean(cnt == 0)]
+        assert np.allclose(m, exp, rtol=1e-10, atol=1e-14), f"{score}: {m} vs {exp}"
+
+
+# ---------------------------------------------------------------------------
+# aux-loss-free balance controller
+# ---------------------------------------------------------------------------
+
+def check_bias_update(L) -> None:
+    """One controller step (README, "SigmoidRouter", step_bias_update):
+    balanced counts leave the bias bitwise unchanged (p = 1/E exactly);
+    a collapse onto expert 0 lowers its bias by (1 - 1/E) rate and raises
+    every starved expert by (1/E + 0.5) rate; a load of exactly 10% of the
+    fair share is not starved (strict <), one token less is; no tokens at
+    all count as starved everywhere (total clamped to 1); the result is
+    clamped to [-10, 10]; and repeated steps balance a skewed router."""
+    rate = 1e-3
+    for E in (6, 7, 16):
+        b = np.linspace(-0.3, 0.3, E).astype(np.float32)
+        nb = oracle.bias_update(np.full(E, 37, np.int32), b, rate, L=L)
+        assert np.array_equal(nb, b), f"E={E}: balanced counts changed the bias"
+        c = np.zeros(E, np.int32)
+        c[0] = 1000
+        nb = oracle.bias_update(c, b, rate, L=L).astype(np.float64)
+        ref = b.astype(np.float64) + rate * np.concatenate([[1.0 / E - 1.0], np.full(E - 1, 1.0 / E + 0.5)])
+        assert np.allclose(nb, ref, rtol=0, atol=1e-7), f"E={E}: collapse step {nb} vs {ref}"
+        z = oracle.bias_update(np.zeros(E, np.int32), b, rate, L=L).astype(np.float64)
+        assert np.allclose(z, b + rate * (1.0 / E + 0.5), rtol=0, atol=1e-7)
+    # starvation threshold: E = 10, 100 tokens; fair share 10, 10% of it is 1 token
+    c = np.array([1, 0, 11, 11, 11, 11, 11, 11, 11, 22], np.int32)
+    nb = oracle.bias_update(c, np.zeros(10, np.float32), 1.0, L=L).astype(np.float64)
+    assert abs(nb[0] - (0.1 - 0.01)) < 1e-6, f"a load of 10% of fair share counted as starved: {nb[0]}"
+    assert abs(nb[1] - (0.1 + 0.5)) < 1e-6, f"an empty expert not boosted: {nb[1]}"
+    assert abs(nb[9] - (0.1 - 0.22)) < 1e-6
+    # clamp
+    nb = oracle.bias_update(c, np.float32([9.9, 9.9, -9.99, 0, 0, 0, 0, 0, 0, -9.99]), 5.0, L=L)
+    assert nb[0] == np.float32(9.9 + 5.0 * np.float32(0.09)) or nb[0] == 10.0
+    assert nb[1] == 10.0 and nb[9] == -10.0 and nb[2] >= -10.0
+    # the controller balances a router skewed towards low ids
+    cfg = LayerConfig("ctl", T=512, d_model=64, n_experts=8, top_k=2, d_ff=64, score="sigmoid", zipf_s=1.5,
+                      seed=5)
+    inp = make_layer(cfg)
+    bias = np.zeros(8, np.float32)
+    first = None
+    for step in range(40):
+        r = oracle.route(inp["x"], inp["w_router"], bias, 2, "sigmoid", True, L=L)
+        cv = np.std(r["counts"].astype(np.float64)) / np.mean(r["counts"])
+        first = cv if first is None else first
+        bias = oracle.bias_update(r["counts"], bias, 0.1, L=L)
+    assert first > 1.0 and cv < 0.05, f"controller did not balance: cv {first:.3f} -> {cv:.3f}"
+
+
 ALL_CHECKS = [check_cexpf, check_logits, check_topk_bruteforce, check_topk_lexsort, check_weights,
-              check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu, check_envelope]
+              check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu, check_envelope,
+              check_route_options, check_router_metrics, check_bias_update]

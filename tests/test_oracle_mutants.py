@@ -27,6 +27,18 @@ MUTANTS = {
                               "                w[j] = w[j] / s;"),
     "softmax_bias_on_logits": ("v[e] = oracle_cexpf(l[e] - m) / z + bias[e];", "v[e] = l[e] + bias[e];"),
     "gate_up_swapped_roles": ("double h = silu(g[b]) * u[b];", "double h = silu(u[b]) * g[b];"),
+    "bias_update_starved_le": ("if (p < starved)", "if (p <= starved)"),
+    "bias_update_sign": ("float err = target - p;", "float err = p - target;"),
+    "bias_update_no_upper_clamp": ("        if (bias[e] > 10.0f)\n            bias[e] = 10.0f;\n", ""),
+    "bias_update_boost_dropped": ("err = err + 0.5f;", "err = err + 0.0f;"),
+    "metrics_cv_biased_std": ("sqrt(var / (double)(E - 1))", "sqrt(var / (double)E)"),
+    "metrics_entropy_unnormalised": ("double p = (P[e] > 1e-9 ? P[e] : 1e-9) / psum;",
+                                     "double p = (P[e] > 1e-9 ? P[e] : 1e-9);"),
+    "metrics_aux_fraction_of_pairs": ("aux += (cnt[e] / (double)T) * P[e];",
+                                      "aux += (cnt[e] / (double)(T * k)) * P[e];"),
+    "metrics_z_without_max": ("lse = m + log(s);", "lse = log(s);"),
+    "logit_bias_dropped": ("            v[e] = l[e] + bias[e];\n", "            v[e] = l[e];\n"),
+    "noise_dropped": ("v[e] = v[e] + noise[e];", "v[e] = v[e] + 0.0f;"),
     "count_off_by_one": ("        counts[idx[t]]++;\n    if (!logits_out)",
                          "        counts[idx[t] == 0 ? 1 : idx[t]]++;\n    if (!logits_out)"),
 }
