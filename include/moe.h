@@ -88,6 +88,8 @@ typedef struct moe_layer {
     int32_t renorm;      /* nonzero: combine weights renormalised over the k chosen experts */
     int32_t dtype;       /* MOE_F32 or MOE_BF16 */
     int32_t d_ff_shared; /* width of the shared expert; 0 when there is none; multiple of 64 */
+    int32_t bias_on_logits; /* 0: sel_bias is added to the score (PR #930 noaux_tc selection bias);
+                               nonzero: to the logit (README, "SigmoidRouter": logits + bias select) */
     const float *w_router; /* [E, d] fp32 (nn.Linear layout) */
     const float *sel_bias; /* [E] fp32 selection bias, or NULL; moves selection only */
     const void *w_gate;    /* [E, d_ff, d]  (w1) */
@@ -97,6 +99,38 @@ typedef struct moe_layer {
     const void *ws_up;     /* [d_ff_shared, d] or NULL */
     const void *ws_down;   /* [d, d_ff_shared] or NULL */
 } moe_layer;
+
+/* Router losses and health metrics (README, "SigmoidRouter": z_loss,
+ * aux_loss, router_cv, router_entropy_bits; PR #931, "What to watch":
+ * moe/load_max_ratio and the share of experts that receive no token).
+ * Indices into the fp64 metrics array of moe_route_opts:
+ *   Z_LOSS        mean over tokens of logsumexp(logits)^2
+ *   AUX_LOSS      E * sum_e f_e P_e, f_e = counts_e / T, P_e = mean unbiased score of e
+ *   CV            unbiased std(counts) / max(mean(counts), 1); 0 when E = 1
+ *   ENTROPY_BITS  -sum p log2 p over p = max(P, 1e-9), normalised to sum 1
+ *   LOAD_MAX_RATIO max(counts) / mean(counts)
+ *   UNUSED_FRAC   share of experts with counts = 0
+ * Scores are the sigmoid or the softmax over all experts, never biased. */
+#define MOE_METRIC_Z_LOSS 0
+#define MOE_METRIC_AUX_LOSS 1
+#define MOE_METRIC_CV 2
+#define MOE_METRIC_ENTROPY_BITS 3
+#define MOE_METRIC_LOAD_MAX_RATIO 4
+#define MOE_METRIC_UNUSED_FRAC 5
+#define MOE_N_METRICS 6
+
+/* Per-call router options for training-time use; a NULL moe_route_opts*
+ * means both off.
+ *   sel_noise  [T, E] fp32 DEVICE array or NULL: added to every selection
+ *              value after the bias (README, "SigmoidRouter": exploration
+ *              noise during training, none at evaluation). The caller draws
+ *              it (randn * std); the library draws no random numbers.
+ *   metrics    [MOE_N_METRICS] fp64 DEVICE array or NULL: written with the
+ *              router metrics of this call, bitwise repeatable. */
+typedef struct moe_route_opts {
+    const float *sel_noise;
+    double *metrics;
+} moe_route_opts;
 
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_str(moe_status s);
@@ -114,12 +148,31 @@ moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
  *   ws       workspace of at least moe_workspace_size bytes (required when T > 0)
  * Selection value: the logit when sel_bias is NULL; otherwise the score plus
  * the bias (sigmoid: 1/(1+exp(-l)); softmax: exp(l-m)/sum exp(l-m), summed in
- * expert order). Weights: softmax renorm exp(l_j - M)/sum_i exp(l_i - M) over
- * the chosen logits; sigmoid renorm s_j/(sum_i s_i + 1e-9); without renorm the
- * score itself. T = 0 zeroes counts.
+ * expert order), or the logit plus the bias when layer->bias_on_logits.
+ * Weights: softmax renorm exp(l_j - M)/sum_i exp(l_i - M) over the chosen
+ * logits; sigmoid renorm s_j/(sum_i s_i + 1e-9); without renorm the score
+ * itself. T = 0 zeroes counts.
  */
 moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, int32_t *topk_idx, float *topk_w,
                      int32_t *counts, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_route with training options (noise, metrics; opts may be NULL).
+ * opts->metrics needs T > 0 (MOE_ERR_INVALID otherwise). */
+moe_status moe_route_ex(const moe_layer *layer, const void *x, int64_t T, const moe_route_opts *opts,
+                        int32_t *topk_idx, float *topk_w, int32_t *counts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One step of the aux-loss-free balance controller (README, "SigmoidRouter",
+ * step_bias_update; PR #930, "Tests": the update is applied after the
+ * forward pass, so the next pass selects with the new bias). In fp32:
+ *   p_e = counts_e / max(sum counts, 1);  err_e = 1/E - p_e;
+ *   err_e += 0.5 where p_e < 0.1/E (starved expert);
+ *   bias_e = clamp(bias_e + err_e * rate, -10, 10).
+ *   counts [n_experts] int32 DEVICE (e.g. from moe_forward; summed over all
+ *          data-parallel ranks by the caller first)
+ *   bias   [n_experts] fp32 DEVICE, updated in place (the layer's sel_bias)
+ */
+moe_status moe_bias_update(int32_t n_experts, const int32_t *counts, float rate, float *bias, void *stream);
 
 /*
  * Dispatch into expert-contiguous order ("SigmoidRouter" one-hot counts;
@@ -179,13 +232,22 @@ moe_status moe_combine(const moe_layer *layer, int64_t T, const float *y_perm, c
 moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T, float *y, int32_t *topk_idx,
                        float *topk_w, int32_t *counts, void *ws, size_t ws_bytes, void *stream);
 
+typedef struct moe_timing moe_timing; /* opaque: one hipEvent per phase boundary */
+
+/* moe_forward with router options (opts may be NULL) and, when `timing` is
+ * not NULL, an event recorded on `stream` at every phase boundary (see
+ * moe_timing_read). */
+moe_status moe_forward_ex(const moe_layer *layer, const void *x, int64_t T, const moe_route_opts *opts, float *y,
+                          int32_t *topk_idx, float *topk_w, int32_t *counts, void *ws, size_t ws_bytes,
+                          void *stream, moe_timing *timing);
+
 /* ---------------------------------------------------------------------- */
 /* Phase timing (measurement only)                                         */
 /* ---------------------------------------------------------------------- */
 
 /* Phases of moe_forward, in launch order. */
 #define MOE_PHASE_ROUTE 0          /* gate product, scores, top-k, weights, block histograms */
-#define MOE_PHASE_SCAN 1           /* counts, offsets, per-block bases, GEMM tile list */
+#define MOE_PHASE_SCAN 1           /* counts, offsets, per-block bases, GEMM tile list, router metrics */
 #define MOE_PHASE_SCATTER 2        /* row_of and the row -> token map */
 #define MOE_PHASE_GATEUP 3         /* routed gate/up grouped GEMM with the SwiGLU epilogue */
 #define MOE_PHASE_DOWN 4           /* routed down grouped GEMM */
@@ -194,18 +256,11 @@ moe_status moe_forward(const moe_layer *layer, const void *x, int64_t T, float *
 #define MOE_PHASE_COMBINE 7        /* weighted combine */
 #define MOE_N_PHASES 8
 
-typedef struct moe_timing moe_timing; /* opaque: one hipEvent per phase boundary */
-
 /* Create / destroy a timing record (creates hipEvents on the current device). */
 moe_status moe_timing_create(moe_timing **out);
 moe_status moe_timing_destroy(moe_timing *t);
 
-/* moe_forward, recording an event on `stream` at every phase boundary. */
-moe_status moe_forward_timed(const moe_layer *layer, const void *x, int64_t T, float *y, int32_t *topk_idx,
-                             float *topk_w, int32_t *counts, void *ws, size_t ws_bytes, void *stream,
-                             moe_timing *t);
-
-/* Milliseconds spent in each phase by the last moe_forward_timed call that
+/* Milliseconds spent in each phase by the last moe_forward_ex call that
  * used `t`; waits for its events. phase_ms: host array of MOE_N_PHASES. */
 moe_status moe_timing_read(moe_timing *t, float *phase_ms);
 

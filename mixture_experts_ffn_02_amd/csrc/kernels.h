@@ -19,10 +19,19 @@ struct RouteLaunch {
   int32_t* hist;          // [n_blocks, E] or null
   int32_t* rank;          // [T, k] or null (needs hist)
   float* logits;          // [T, E] scratch for the small-batch split path, or null (always fused)
+  int bias_on_logits;     // nonzero: selection value = logit + bias (else score + bias)
+  const float* noise;     // [T, E] added to the selection value, or null
+  double* mpart;          // [n_blocks, E + 1] metric partials (score sums, sum of lse^2), or null
 };
 int route_tokens_per_block(int E);
 size_t route_lds_bytes(int E, int k);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+// out[6] = z-loss, aux loss, cv, entropy (bits), max/mean load, unused share,
+// from the partials of launch_route (nb blocks) and the expert counts.
+hipError_t launch_router_metrics(const double* mpart, int nb, const int32_t* counts, int64_t T, int E, int k,
+                                 double* out, hipStream_t s);
+// One step of the balance controller on bias [E] from counts [E].
+hipError_t launch_bias_update(const int32_t* counts, int E, float rate, float* bias, hipStream_t s);
 
 // --------------------------------------------------------------- dispatch
 // Per-block expert histograms and ranks from expert ids (no routing).

@@ -44,7 +44,8 @@ moe_status check_layer(const moe_layer* L, bool need_experts) {
 }
 
 struct Layout {
-  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, logits, h, yperm, hs, ys, total;
+  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, logits, mpart, h, yperm, hs,
+      ys, total;
   int64_t nb;         // histogram rows (blocks)
   int64_t max_tiles;  // bound on grouped GEMM row tiles
 };
@@ -77,6 +78,7 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   o.idx = take(sizeof(int32_t) * (size_t)rows);
   o.w = take(sizeof(float) * (size_t)rows);
   o.logits = take(sizeof(float) * (size_t)(T * E));
+  o.mpart = take(sizeof(double) * (size_t)(o.nb * (E + 1)));
   o.h = take((size_t)eb * (size_t)(rows * f));
   o.yperm = take(sizeof(float) * (size_t)(rows * d));
   o.hs = take((size_t)eb * (size_t)(T * fs));
@@ -116,11 +118,31 @@ moe_status check_T(int64_t T, int k) {
   return MOE_OK;
 }
 
-moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* idx, float* w,
-                        int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s, moe_timing* tm) {
+// Options: noise must be 16-byte aligned device data; metrics need tokens.
+moe_status check_opts(const moe_route_opts* o, int64_t T) {
+  if (!o) return MOE_OK;
+  if (o->sel_noise && !aligned16(o->sel_noise)) return MOE_ERR_INVALID;
+  if (o->metrics && (T <= 0 || ((uintptr_t)o->metrics & 7u))) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+RouteLaunch route_launch(const moe_layer* L, const void* x, int64_t T, const moe_route_opts* o, int32_t* idx,
+                         float* w, int32_t* hist, int32_t* rank, void* ws, const Layout& lo) {
+  RouteLaunch r{x, L->dtype, T, L->d_model, L->n_experts, L->top_k, L->score, L->renorm, L->w_router, L->sel_bias,
+                idx, w, hist, rank, at<float>(ws, lo.logits)};
+  r.bias_on_logits = L->bias_on_logits;
+  r.noise = o ? o->sel_noise : nullptr;
+  r.mpart = (o && o->metrics) ? at<double>(ws, lo.mpart) : nullptr;
+  return r;
+}
+
+moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_route_opts* opts, float* y,
+                        int32_t* idx, float* w, int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s,
+                        moe_timing* tm) {
   moe_status st = check_layer(L, true);
   if (st != MOE_OK) return st;
   if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if ((st = check_opts(opts, T)) != MOE_OK) return st;
   if (T > 0 && (!x || !y || !aligned16(x) || !aligned16(y))) return MOE_ERR_INVALID;
   if ((idx && !aligned16(idx)) || (w && !aligned16(w))) return MOE_ERR_INVALID;
   const Layout lo = make_layout(L, T);
@@ -148,11 +170,11 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, float* y, 
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
   mark(tm, MOE_PHASE_ROUTE, s);
-  RouteLaunch r{x, L->dtype, T, d, E, k, L->score, L->renorm, L->w_router, L->sel_bias, idx_p, w_p, hist, rank,
-                at<float>(ws, lo.logits)};
+  const RouteLaunch r = route_launch(L, x, T, opts, idx_p, w_p, hist, rank, ws, lo);
   MOE_TRY(launch_route(r, s));
   mark(tm, MOE_PHASE_SCAN, s);
   MOE_TRY(launch_scan(hist, (int)nb_route, E, counts_p, offsets, base, bm, n_tiles, tiles, s));
+  if (r.mpart) MOE_TRY(launch_router_metrics(r.mpart, (int)nb_route, counts_p, T, E, k, opts->metrics, s));
   mark(tm, MOE_PHASE_SCATTER, s);
   MOE_TRY(launch_scatter(idx_p, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s));
 
@@ -248,9 +270,16 @@ moe_status moe_workspace_size(const moe_layer* L, int64_t T, size_t* bytes) {
 
 moe_status moe_route(const moe_layer* L, const void* x, int64_t T, int32_t* topk_idx, float* topk_w,
                      int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  return moe_route_ex(L, x, T, nullptr, topk_idx, topk_w, counts, ws, ws_bytes, stream);
+}
+
+moe_status moe_route_ex(const moe_layer* L, const void* x, int64_t T, const moe_route_opts* opts,
+                        int32_t* topk_idx, float* topk_w, int32_t* counts, void* ws, size_t ws_bytes,
+                        void* stream) {
   moe_status st = check_layer(L, false);
   if (st != MOE_OK) return st;
   if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  if ((st = check_opts(opts, T)) != MOE_OK) return st;
   if (T > 0 && (!x || !topk_idx || !topk_w || !aligned16(x))) return MOE_ERR_INVALID;
   const Layout lo = make_layout(L, T);
   if (T > 0 && (!ws || ws_bytes < lo.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
@@ -260,14 +289,24 @@ moe_status moe_route(const moe_layer* L, const void* x, int64_t T, int32_t* topk
     if (counts) MOE_TRY(launch_fill_i32(counts, L->n_experts, 0, s));
     return MOE_OK;
   }
-  int32_t* hist = counts ? at<int32_t>(ws, lo.hist) : nullptr;
-  RouteLaunch r{x, L->dtype, T, L->d_model, L->n_experts, L->top_k, L->score, L->renorm, L->w_router,
-                L->sel_bias, topk_idx, topk_w, hist, nullptr, at<float>(ws, lo.logits)};
+  // metrics need the counts: kept in the workspace when the caller wants none
+  const bool metrics = opts && opts->metrics;
+  int32_t* counts_p = counts ? counts : (metrics ? at<int32_t>(ws, lo.counts) : nullptr);
+  int32_t* hist = counts_p ? at<int32_t>(ws, lo.hist) : nullptr;
+  const RouteLaunch r = route_launch(L, x, T, opts, topk_idx, topk_w, hist, nullptr, ws, lo);
   MOE_TRY(launch_route(r, s));
-  if (counts) {
-    const int tpb = route_tokens_per_block(L->n_experts);
-    MOE_TRY(launch_counts(hist, (int)((T + tpb - 1) / tpb), L->n_experts, counts, s));
-  }
+  const int tpb = route_tokens_per_block(L->n_experts);
+  const int nb = (int)((T + tpb - 1) / tpb);
+  if (counts_p) MOE_TRY(launch_counts(hist, nb, L->n_experts, counts_p, s));
+  if (metrics) MOE_TRY(launch_router_metrics(r.mpart, nb, counts_p, T, L->n_experts, L->top_k, opts->metrics, s));
+  return MOE_OK;
+}
+
+moe_status moe_bias_update(int32_t n_experts, const int32_t* counts, float rate, float* bias, void* stream) {
+  if (n_experts < 1 || !counts || !bias) return MOE_ERR_INVALID;
+  if (n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  MOE_TRY(launch_bias_update(counts, n_experts, rate, bias, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -376,7 +415,13 @@ moe_status moe_combine(const moe_layer* L, int64_t T, const float* y_perm, const
 
 moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(L, x, T, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, nullptr);
+  return forward_impl(L, x, T, nullptr, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_forward_ex(const moe_layer* L, const void* x, int64_t T, const moe_route_opts* opts, float* y,
+                          int32_t* topk_idx, float* topk_w, int32_t* counts, void* ws, size_t ws_bytes, void* stream,
+                          moe_timing* timing) {
+  return forward_impl(L, x, T, opts, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, timing);
 }
 
 moe_status moe_timing_create(moe_timing** out) {
@@ -399,13 +444,6 @@ moe_status moe_timing_destroy(moe_timing* t) {
   for (int i = 0; i <= MOE_N_PHASES; ++i) (void)hipEventDestroy(t->ev[i]);
   delete t;
   return MOE_OK;
-}
-
-moe_status moe_forward_timed(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx,
-                             float* topk_w, int32_t* counts, void* ws, size_t ws_bytes, void* stream,
-                             moe_timing* t) {
-  if (!t) return MOE_ERR_INVALID;
-  return forward_impl(L, x, T, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, t);
 }
 
 moe_status moe_timing_read(moe_timing* t, float* phase_ms) {

@@ -273,9 +273,8 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   __syncthreads();
   }
 
-  const bool need_z = (p.score == 0) && (p.bias != nullptr || !p.renorm);
-  if (need_z) {
-    // softmax normaliser per token: max, then sum of exp over experts ascending
+  // softmax normaliser per token: max, then sum of exp over experts ascending
+  auto normalisers = [&]() {
     for (int tt = tid; tt < TT; tt += 256) {
       const float* l = lg + tt * (EP + 1);
       float m = l[0];
@@ -286,7 +285,9 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
       tok_z[tt] = z;
     }
     __syncthreads();
-  }
+  };
+  const bool need_z = (p.score == 0) && ((p.bias != nullptr && !p.bias_on_logits) || !p.renorm);
+  if (need_z) normalisers();
 
   // ---- top-k: a group of G lanes per token, VPL values per lane
   {
@@ -296,7 +297,9 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int gi = lane / G, li = lane % G;
     const bool has_bias = p.bias != nullptr;
+    const bool logit_bias = p.bias_on_logits != 0;
     const bool sigmoid = p.score == 1;
+    const float* __restrict__ noise = p.noise;
     for (int base = 0; base < TT; base += 4 * TPW) {
       const int tt = base + wave * TPW + gi;
       const float* l = lg + tt * (EP + 1);
@@ -308,8 +311,12 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
         if (e < E) {
           float v = l[e];
           if (has_bias) {
-            v = sigmoid ? sigmoid_canon(v) + bias_s[e] : canonical_exp(v - tok_m[tt]) / tok_z[tt] + bias_s[e];
+            if (logit_bias)
+              v = v + bias_s[e];
+            else
+              v = sigmoid ? sigmoid_canon(v) + bias_s[e] : canonical_exp(v - tok_m[tt]) / tok_z[tt] + bias_s[e];
           }
+          if (noise && tt < tt_count) v = v + noise[(t0 + tt) * E + e];
           key[q] = topk_key(v, e);
         }
       }
@@ -365,9 +372,128 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
     }
   }
 
+  // ---- metric partials of this block: per-expert sums of the unbiased
+  // scores over its tokens (ascending token order) and the sum of lse^2
+  if (p.mpart) {
+    __syncthreads();
+    if (!need_z) normalisers();
+    double* row = p.mpart + (size_t)blockIdx.x * (E + 1);
+    for (int e = tid; e < E; e += 256) {
+      double acc = 0.0;
+      for (int tt = 0; tt < tt_count; ++tt) {
+        const float l = lg[tt * (EP + 1) + e];
+        acc += (double)(p.score == 1 ? sigmoid_canon(l) : canonical_exp(l - tok_m[tt]) / tok_z[tt]);
+      }
+      row[e] = acc;
+    }
+    if (tid == 255) {
+      double acc = 0.0;
+      for (int tt = 0; tt < tt_count; ++tt) {
+        const double lse = (double)tok_m[tt] + (double)logf(tok_z[tt]);
+        acc += lse * lse;
+      }
+      row[E] = acc;
+    }
+  }
+
   if (p.hist) {
     block_hist_rank(sel, tt_count, k, E, W, masks, p.hist + (size_t)blockIdx.x * E,
                     p.rank ? p.rank + t0 * k : nullptr);
+  }
+}
+
+// Router losses and health metrics from the per-block partials and the
+// counts (one block of 1024 threads; every sum runs in a fixed order, so the
+// result is bitwise repeatable):
+//   P_e = (sum over blocks of the score sums) / T
+//   z-loss = (sum of lse^2) / T; aux = E sum_e (c_e / T) P_e;
+//   cv = unbiased std(c) / max(mean(c), 1); entropy = -sum p log2 p over
+//   p = max(P, 1e-9) normalised; max/mean load; share of experts with c = 0.
+__global__ __launch_bounds__(1024) void k_router_metrics(const double* __restrict__ mpart, int nb,
+                                                         const int32_t* __restrict__ counts, int64_t T, int E, int k,
+                                                         double* __restrict__ out) {
+  __shared__ double part[16][64];
+  __shared__ double P[1025];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // column sums: lane = column within a chunk of 64, wave = row phase
+  for (int c0 = 0; c0 <= E; c0 += 64) {
+    const int c = c0 + lane;
+    double s = 0.0;
+    if (c <= E)
+      for (int b = wave; b < nb; b += 16) s += mpart[(size_t)b * (E + 1) + c];
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && c <= E) {
+      double t = 0.0;
+      for (int w = 0; w < 16; ++w) t += part[w][lane];
+      P[c] = t;
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  const double Td = (double)T;
+  const double mean = (double)(T * k) / (double)E;
+  double aux = 0.0, var = 0.0, mx = 0.0, unused = 0.0, psum = 0.0;
+  for (int e = lane; e < E; e += 64) {
+    const double pe = P[e] / Td, c = (double)counts[e];
+    aux += (c / Td) * pe;
+    var += (c - mean) * (c - mean);
+    mx = c > mx ? c : mx;
+    unused += c == 0.0 ? 1.0 : 0.0;
+    psum += pe > 1e-9 ? pe : 1e-9;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    aux += __shfl_xor(aux, off);
+    var += __shfl_xor(var, off);
+    const double o = __shfl_xor(mx, off);
+    mx = o > mx ? o : mx;
+    unused += __shfl_xor(unused, off);
+    psum += __shfl_xor(psum, off);
+  }
+  double ent = 0.0;
+  for (int e = lane; e < E; e += 64) {
+    const double pe = P[e] / Td;
+    const double q = (pe > 1e-9 ? pe : 1e-9) / psum;
+    ent -= q * log(q);
+  }
+  for (int off = 32; off > 0; off >>= 1) ent += __shfl_xor(ent, off);
+  if (lane == 0) {
+    out[0] = P[E] / Td;
+    out[1] = (double)E * aux;
+    out[2] = E > 1 ? sqrt(var / (double)(E - 1)) / (mean > 1.0 ? mean : 1.0) : 0.0;
+    out[3] = ent / log(2.0);
+    out[4] = mean > 0.0 ? mx / mean : 0.0;
+    out[5] = unused / (double)E;
+  }
+}
+
+// One step of the aux-loss-free balance controller (README,
+// "SigmoidRouter", step_bias_update), in fp32 in the order of that code:
+// p = c / max(sum c, 1); err = 1/E - p, plus 0.5 where p < 0.1/E;
+// bias += err * rate; bias clamped to [-10, 10]. The sum of counts is exact
+// integer arithmetic; 1/E and 0.1/E are formed in fp64 and rounded once.
+__global__ __launch_bounds__(256) void k_bias_update(const int32_t* __restrict__ counts, int E, float rate,
+                                                     float* __restrict__ bias) {
+  __shared__ long long part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long s = 0;
+  for (int e = tid; e < E; e += 256) s += counts[e];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) part[wave] = s;
+  __syncthreads();
+  const long long sum = part[0] + part[1] + part[2] + part[3];
+  float total = (float)sum;
+  if (total < 1.0f) total = 1.0f;
+  const float target = (float)(1.0 / (double)E);
+  const float starved = (float)(0.1 * (1.0 / (double)E));
+  for (int e = tid; e < E; e += 256) {
+    const float pe = (float)counts[e] / total;
+    float err = target - pe;
+    if (pe < starved) err = err + 0.5f;
+    float b = bias[e] + err * rate;
+    b = b < -10.0f ? -10.0f : b;
+    b = b > 10.0f ? 10.0f : b;
+    bias[e] = b;
   }
 }
 
@@ -546,6 +672,19 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
     case 1024: return launch_route_ep<1024>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_router_metrics(const double* mpart, int nb, const int32_t* counts, int64_t T, int E, int k,
+                                 double* out, hipStream_t s) {
+  if (T <= 0 || E > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_router_metrics, dim3(1), dim3(1024), 0, s, mpart, nb, counts, T, E, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float rate, float* bias, hipStream_t s) {
+  if (E <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bias_update, dim3(1), dim3(256), 0, s, counts, E, rate, bias);
+  return hipGetLastError();
 }
 
 int hist_tokens_per_block() { return kHistTT; }

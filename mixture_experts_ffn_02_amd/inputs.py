@@ -37,7 +37,7 @@ from typing import Dict, Optional
 import numpy as np
 
 # Stream ids of the tensors of one layer.
-TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD, TID_SG, TID_SU, TID_SD = range(9)
+TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD, TID_SG, TID_SU, TID_SD, TID_NOISE = range(10)
 X_CHUNK_ROWS = 1024
 
 
@@ -57,6 +57,7 @@ class LayerConfig:
     shared: bool = False           # one always-on shared SwiGLU expert
     d_ff_shared: int = 0           # 0: same width as a routed expert
     bias_range: float = 0.0        # selection bias ~ U(-r, r); 0: no bias
+    bias_on_logits: bool = False   # the bias enters the logit instead of the score
     weight_std: Optional[float] = None  # None: 1/sqrt(fan_in) for every weight
     zipf_s: float = 0.0            # > 0: skew the router towards low expert ids
     seed: int = 0
@@ -194,3 +195,9 @@ def make_layer(cfg: LayerConfig, T: Optional[int] = None, with_experts: bool = T
             else:
                 out["ws_gate"] = out["ws_up"] = out["ws_down"] = None
     return out
+
+
+def make_noise(cfg: LayerConfig, std: float, step: int = 0, T: Optional[int] = None) -> np.ndarray:
+    """Router exploration noise [T, n_experts] fp32: N(0, std), one stream per step."""
+    T = cfg.T if T is None else T
+    return _normal(cfg.seed, TID_NOISE, step, (T, cfg.n_experts), std)

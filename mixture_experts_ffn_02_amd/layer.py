@@ -51,7 +51,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 class Timing:
-    """Per-phase hipEvent timing of moe_forward_timed."""
+    """Per-phase hipEvent timing of moe_forward_ex."""
 
     def __init__(self):
         self.lib = N.load()
@@ -89,6 +89,7 @@ class MoELayer:
         c.renorm = int(bool(cfg.renorm))
         c.dtype = N.MOE_BF16 if cfg.dtype == "bf16" else N.MOE_F32
         c.d_ff_shared = cfg.d_ff_s
+        c.bias_on_logits = int(bool(cfg.bias_on_logits))
         for name in ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
             tt = tensors.get(name)
             setattr(c, name, None if tt is None else tt.data_ptr())
@@ -114,6 +115,19 @@ class MoELayer:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
+    def _opts(self, T: int, noise: Optional[torch.Tensor], metrics: bool):
+        """moe_route_opts for one call, and the metrics tensor it fills."""
+        if noise is None and not metrics:
+            return None, None
+        if noise is not None and (noise.shape != (T, self.cfg.n_experts) or noise.dtype != torch.float32
+                                  or not noise.is_contiguous()):
+            raise ValueError(f"noise must be contiguous fp32 [T, {self.cfg.n_experts}]")
+        m = torch.empty(N.MOE_N_METRICS, dtype=torch.float64, device=self.device) if metrics else None
+        o = N.MoeRouteOptsC()
+        o.sel_noise = None if noise is None else noise.data_ptr()
+        o.metrics = None if m is None else m.data_ptr()
+        return o, m
+
     def _check_x(self, x: torch.Tensor) -> int:
         if x.dim() != 2 or x.shape[1] != self.cfg.d_model or not x.is_contiguous():
             raise ValueError(f"x must be contiguous [T, {self.cfg.d_model}]")
@@ -123,7 +137,11 @@ class MoELayer:
 
     # ---------------------------------------------------------- entry points
     def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, want_routing: bool = True,
-                timing: Optional[Timing] = None) -> Dict[str, torch.Tensor]:
+                timing: Optional[Timing] = None, noise: Optional[torch.Tensor] = None,
+                metrics: bool = False) -> Dict[str, torch.Tensor]:
+        """y = the layer applied to x; with want_routing also idx, w and counts;
+        noise [T, E] fp32 is added to the selection values; metrics: the
+        router losses and health metrics (fp64 [6], order of METRICS)."""
         T = self._check_x(x)
         k, E, d = self.cfg.top_k, self.cfg.n_experts, self.cfg.d_model
         dev = x.device
@@ -137,23 +155,45 @@ class MoELayer:
             counts = torch.empty((E,), dtype=torch.int32, device=dev)
             out.update(idx=idx, w=w, counts=counts)
         ws = self.workspace(T)
-        args = (ctypes.byref(self.c), _p(x), T, _p(y), _p(idx), _p(w), _p(counts), _p(ws), ws.numel(), _stream())
-        if timing is None:
-            N.check(self.lib.moe_forward(*args), "moe_forward")
+        opts, m = self._opts(T, noise, metrics)
+        if opts is None and timing is None:
+            N.check(self.lib.moe_forward(ctypes.byref(self.c), _p(x), T, _p(y), _p(idx), _p(w), _p(counts), _p(ws),
+                                         ws.numel(), _stream()), "moe_forward")
         else:
-            N.check(self.lib.moe_forward_timed(*args, timing.h), "moe_forward_timed")
+            N.check(self.lib.moe_forward_ex(ctypes.byref(self.c), _p(x), T, None if opts is None else ctypes.byref(opts),
+                                            _p(y), _p(idx), _p(w), _p(counts), _p(ws), ws.numel(), _stream(),
+                                            None if timing is None else timing.h), "moe_forward_ex")
+        if m is not None:
+            out["metrics"] = m
         return out
 
-    def route(self, x: torch.Tensor) -> Dict[str, torch.Tensor]:
+    def route(self, x: torch.Tensor, noise: Optional[torch.Tensor] = None,
+              metrics: bool = False) -> Dict[str, torch.Tensor]:
         T = self._check_x(x)
         k, E = self.cfg.top_k, self.cfg.n_experts
         idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
         w = torch.empty((T, k), dtype=torch.float32, device=x.device)
         counts = torch.empty((E,), dtype=torch.int32, device=x.device)
         ws = self.workspace(T)
-        N.check(self.lib.moe_route(ctypes.byref(self.c), _p(x), T, _p(idx), _p(w), _p(counts), _p(ws), ws.numel(),
-                                   _stream()), "moe_route")
-        return {"idx": idx, "w": w, "counts": counts}
+        opts, m = self._opts(T, noise, metrics)
+        if opts is None:
+            N.check(self.lib.moe_route(ctypes.byref(self.c), _p(x), T, _p(idx), _p(w), _p(counts), _p(ws),
+                                       ws.numel(), _stream()), "moe_route")
+        else:
+            N.check(self.lib.moe_route_ex(ctypes.byref(self.c), _p(x), T, ctypes.byref(opts), _p(idx), _p(w),
+                                          _p(counts), _p(ws), ws.numel(), _stream()), "moe_route_ex")
+        out = {"idx": idx, "w": w, "counts": counts}
+        if m is not None:
+            out["metrics"] = m
+        return out
+
+    def bias_update(self, counts: torch.Tensor, rate: float) -> torch.Tensor:
+        """One balance-controller step on this layer's selection bias, in place."""
+        b = self.t.get("sel_bias")
+        if b is None:
+            raise ValueError("the layer has no selection bias")
+        bias_update(counts, b, rate)
+        return b
 
     def permute(self, x: torch.Tensor, idx: torch.Tensor, with_rows: bool = True) -> Dict[str, torch.Tensor]:
         T = self._check_x(x)
@@ -175,6 +215,15 @@ class MoELayer:
         N.check(self.lib.moe_combine(ctypes.byref(self.c), T, _p(y_perm), _p(row_of), _p(w), _p(y_shared), _p(y),
                                      _stream()), "moe_combine")
         return y
+
+
+def bias_update(counts: torch.Tensor, bias: torch.Tensor, rate: float) -> None:
+    """moe_bias_update: bias [E] fp32 updated in place from counts [E] int32."""
+    if counts.dtype != torch.int32 or bias.dtype != torch.float32 or counts.numel() != bias.numel():
+        raise ValueError("counts must be int32 [E] and bias fp32 [E]")
+    if not (counts.is_contiguous() and bias.is_contiguous()):
+        raise ValueError("counts and bias must be contiguous")
+    N.check(N.load().moe_bias_update(bias.numel(), _p(counts), float(rate), _p(bias), _stream()), "moe_bias_update")
 
 
 def grouped_swiglu(a: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,

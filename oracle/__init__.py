@@ -205,11 +205,13 @@ def combine(x, tokens, idx, w, w_gate, w_up, w_down, ws_gate=None, ws_up=None, w
 
 
 def forward(inputs: Dict[str, np.ndarray], top_k: int, score: str, renorm: bool = True,
-            tokens: Optional[np.ndarray] = None, L=None) -> Dict[str, np.ndarray]:
+            tokens: Optional[np.ndarray] = None, L=None, bias_on_logits: bool = False,
+            noise: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The whole layer: routing for every token, dispatch order, and the fp64
     output y for ``tokens`` (all tokens when None)."""
     x = inputs["x"]
-    r = route(x, inputs["w_router"], inputs.get("sel_bias"), top_k, score, renorm, L=L)
+    r = route(x, inputs["w_router"], inputs.get("sel_bias"), top_k, score, renorm, L=L,
+              bias_on_logits=bias_on_logits, noise=noise)
     E = inputs["w_router"].shape[0]
     dsp = dispatch(r["idx"], E, L=L)
     if tokens is None:

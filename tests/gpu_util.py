@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import oracle
-from mixture_experts_ffn_02_amd.inputs import LayerConfig, make_layer
+from mixture_experts_ffn_02_amd.inputs import CONFIGS, LayerConfig, make_layer
 from mixture_experts_ffn_02_amd.layer import MoELayer, to_device, to_host
 
 # Output tolerance: max|err| <= TOL * RMS(y_oracle).
@@ -84,3 +84,20 @@ def assert_output(cfg: LayerConfig, y_gpu: np.ndarray, y_ref: np.ndarray, what="
     assert np.isfinite(y_gpu).all(), f"{what}: non-finite output"
     assert err <= tol * r, f"{what}: max|err| {err:.3e} > {tol} * RMS {r:.3e} (ratio {err / r:.3e})"
     return err / r
+
+
+def check_y(cfg, inp, o, y_gpu, tokens=None):
+    """fp32 layers: max|err| <= 1e-5 RMS(y). bf16 layers: every element within
+    the bf16-activation envelope; the layers named in the workload table also
+    meet max|err| <= 2e-2 RMS(y). (Narrow test shapes with d_ff of 64 cannot
+    meet the RMS bound with any bf16 activation: a numpy simulation of the
+    rounding alone gives 0.02-0.04 there.)"""
+    y_ref = o["y"]
+    if cfg.dtype == "f32":
+        return assert_output(cfg, y_gpu, y_ref, cfg.name)
+    worst = assert_within_envelope(y_gpu, y_ref, output_envelope(cfg, inp, o, tokens), cfg.name)
+    ratio = rms_ratio(y_gpu, y_ref)
+    print(f"{cfg.name}: max|err|/RMS = {ratio:.3e}, worst error/envelope = {worst:.3f}")
+    if cfg.name in CONFIGS:
+        assert_output(cfg, y_gpu, y_ref, cfg.name)
+    return ratio

@@ -120,4 +120,18 @@ def test_other_entry_points_reject(lib):
     assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, None, p, p, p, p, p, n.value, None) == 1
     assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, p, p, p, p, p, p, n.value - 1, None) == 3
     assert lib.moe_timing_read(None, None) == 1
-    assert lib.moe_forward_timed(ctypes.byref(c), p, 10, p, None, None, None, p, 1 << 40, None, None) == 1
+    # options: misaligned noise, misaligned metrics, metrics without tokens
+    bad_noise = N.MoeRouteOptsC(FAKE + 4, None)
+    bad_metrics = N.MoeRouteOptsC(None, FAKE + 4)
+    metrics = N.MoeRouteOptsC(None, FAKE)
+    for o in (bad_noise, bad_metrics):
+        assert lib.moe_forward_ex(ctypes.byref(c), p, 10, ctypes.byref(o), p, None, None, None, p, 1 << 40, None,
+                                  None) == 1
+        assert lib.moe_route_ex(ctypes.byref(c), p, 10, ctypes.byref(o), p, p, None, p, 1 << 40, None) == 1
+    assert lib.moe_route_ex(ctypes.byref(c), p, 0, ctypes.byref(metrics), p, p, None, p, 1 << 40, None) == 1
+    assert lib.moe_forward_ex(ctypes.byref(c), None, 10, None, p, None, None, None, p, 1 << 40, None, None) == 1
+    # controller: expert count and pointers
+    assert lib.moe_bias_update(0, p, 1e-3, p, None) == 1
+    assert lib.moe_bias_update(8, None, 1e-3, p, None) == 1
+    assert lib.moe_bias_update(8, p, 1e-3, None, None) == 1
+    assert lib.moe_bias_update(1025, p, 1e-3, p, None) == 2
