@@ -106,6 +106,31 @@ __device__ __forceinline__ void mfma_step<float>(f32x16& acc, const u32x4& a, co
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[q]), __uint_as_float(b[q]), acc, 0, 0, 0);
 }
 
+// Scheduling shape of one K step: MFMAs alternating with LDS reads (RD) and
+// DMA issues (VM), as long as either lasts, then the remaining MFMAs.
+template <int MF, int RD, int VM>
+__device__ __forceinline__ void interleave() {
+  constexpr int OTHER = RD + VM;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (i < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read (DMA)
+    if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+  }
+  static_assert(OTHER >= 0, "");
+}
+
+// Output element type: gate/up stores the activation in the operand type,
+// down stores fp32.
+template <typename DT, bool GATEUP>
+struct Out {
+  using T = float;
+};
+template <typename DT>
+struct Out<DT, true> {
+  using T = DT;
+};
+
 template <typename DT>
 __device__ __forceinline__ DT to_out(float v);
 template <>
@@ -263,10 +288,13 @@ void k_gemm(GemmLaunch g) {
 
     // Pipeline: NBUF LDS stages, two fragment sets P and Q alternating over
     // the SPS K steps of a stage (SPS is even, so step 0 always uses P).
-    // Step s < SPS-1: read step s+1 into the other set, MFMAs of step s.
+    // Step s < SPS-1: MFMAs of step s with the LDS reads of step s+1 (into the
+    // other set) interleaved one by one, so the reads complete under the
+    // MFMAs instead of in front of them.
     // Last step: wait for stage kt+1 and for this wave's reads, barrier (every
-    // wave is done with stage kt, so its buffer takes stage kt + NBUF), issue
-    // that stage, read step 0 of stage kt+1 into P, MFMAs of the last step.
+    // wave is done with stage kt, so its buffer takes stage kt + NBUF); then
+    // the MFMAs of the last step with that stage's DMA issues and the reads of
+    // step 0 of stage kt+1 (into P) interleaved.
     Frag P, Q;
 #pragma unroll
     for (int q = 0; q < NBUF; ++q)
@@ -293,51 +321,71 @@ void k_gemm(GemmLaunch g) {
         Frag& nxt = (s & 1) ? P : Q;
         if (s + 1 < C::SPS) {
           load_frag(nxt, kt, s + 1);
+          mma(cur);
+          interleave<C::NG * C::FM * C::FN, C::FM + C::NG * C::FN, 0>();
         } else {
           // stages in flight beyond kt+1: kt+2 .. min(kt+NBUF-1, nk-1)
           const int last = (kt + NBUF - 1 < nk - 1) ? kt + NBUF - 1 : nk - 1;
           wait_stage(last - (kt + 1));
           __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
           if (kt + NBUF < nk) issue(kt + NBUF);
           if (kt + 1 < nk) load_frag(nxt, kt + 1, 0);
+          mma(cur);
+          interleave<C::NG * C::FM * C::FN, C::FM + C::NG * C::FN, C::LPS>();
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mma(cur);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // LDS is reused by the next tile
+    __syncthreads();  // every wave is done with the stage buffers
 
-    // Epilogue. Element e of a 32 x 32 accumulator tile sits in row
-    // 8*(e/4) + 4*(l/32) + e%4 and column l % 32 of lane l. One tile at a
-    // time (scheduling barriers keep the tiles from being interleaved, which
-    // would need more registers than the accumulators leave free).
+    // Epilogue, one 32 x 32 accumulator tile at a time. Element e of a tile
+    // sits in row 8*(e/4) + 4*(l/32) + e%4 and column l % 32 of lane l; the
+    // wave writes the tile (SwiGLU applied, converted to the output type) to
+    // its own LDS scratch, row-major with padded rows, and reads it back as
+    // 16-byte row chunks, so that each store covers contiguous columns.
+    {
+      using OT = typename Out<DT, GATEUP>::T;
+      constexpr int OB = (int)sizeof(OT);
+      constexpr int PITCH = 32 * OB + 16;
+      constexpr int CH = 32 * OB / 16;  // 16-byte chunks per row
+      static_assert(4 * 32 * PITCH <= NBUF * C::STAGE, "epilogue scratch");
+      unsigned char* scr = lds + wave * 32 * PITCH;
+      unsigned char* out = reinterpret_cast<unsigned char*>(g.out);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
+      for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int n = n0 + wn * C::TN + j * 32 + (lane & 31);
-        const int mb = wm * C::TM + i * 32 + 4 * (lane >> 5);
-        if constexpr (GATEUP) {
-          DT* out = reinterpret_cast<DT*>(g.out);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = mb + 8 * (e >> 2) + (e & 3);
-            const float gv = acc[0][i][j][e], uv = acc[1][i][j][e];
-            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-            if (m < rows) out[(size_t)(row0 + m) * g.N + n] = to_out<DT>(hv);
-          }
-        } else {
-          float* out = reinterpret_cast<float*>(g.out);
+        for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int m = mb + 8 * (e >> 2) + (e & 3);
-            if (m < rows) out[(size_t)(row0 + m) * g.N + n] = acc[0][i][j][e];
+            const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            OT v;
+            if constexpr (GATEUP) {
+              const float gv = acc[0][i][j][e], uv = acc[1][i][j][e];
+              v = to_out<DT>(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+            } else {
+              v = acc[0][i][j][e];
+            }
+            *reinterpret_cast<OT*>(scr + r * PITCH + (lane & 31) * OB) = v;
           }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+          for (int q0 = 0; q0 < 32 * CH; q0 += 64) {
+            const int q = q0 + lane, r = q / CH, c16 = q % CH;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(scr + r * PITCH + c16 * 16);
+            const int m = wm * C::TM + i * 32 + r;
+            const int n = n0 + wn * C::TN + j * 32 + c16 * (16 / OB);
+            if (m < rows) *reinterpret_cast<u32x4*>(out + ((size_t)(row0 + m) * g.N + n) * OB) = v;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __syncthreads();  // scratch reads done before the next tile's DMA
   }
 }
 
