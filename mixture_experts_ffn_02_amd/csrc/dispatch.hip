@@ -36,13 +36,27 @@ __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
   return total;
 }
 
-__global__ __launch_bounds__(256) void k_counts(const int32_t* __restrict__ hist, int nb, int E,
-                                                int32_t* __restrict__ counts) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+// counts[e] = sum over blocks of hist[b, e]: one block; thread (g, e) sums
+// rows g, g + R, ... of column e (R = 1024 / E rounded to a power of two),
+// so that the loads of many rows are in flight at once.
+__global__ __launch_bounds__(kScanThreads) void k_counts(const int32_t* __restrict__ hist, int nb, int E,
+                                                         int32_t* __restrict__ counts) {
+  __shared__ int part[kScanThreads];
+  const int tid = threadIdx.x;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int R = kScanThreads / ep;
+  const int g = tid / ep, e = tid % ep;
   int c = 0;
-  for (int b = 0; b < nb; ++b) c += hist[(size_t)b * E + e];
-  counts[e] = c;
+  if (e < E)
+    for (int b = g; b < nb; b += R) c += hist[(size_t)b * E + e];
+  part[tid] = c;
+  __syncthreads();
+  if (tid < E) {
+    int t = 0;
+    for (int gg = 0; gg < R; ++gg) t += part[gg * ep + tid];
+    counts[tid] = t;
+  }
 }
 
 // One block. Thread (g, e) owns expert e over block range g.
@@ -168,7 +182,8 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
 }  // namespace
 
 hipError_t launch_counts(const int32_t* hist, int nb, int E, int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(k_counts, dim3((E + 255) / 256), dim3(256), 0, s, hist, nb, E, counts);
+  if (E > kScanThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_counts, dim3(1), dim3(kScanThreads), 0, s, hist, nb, E, counts);
   return hipGetLastError();
 }
 

@@ -59,7 +59,9 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
 
 // Launch shape per padded expert count EP (power of two, 8..1024):
 //   ME experts x MT tokens per thread, EG expert groups x TG token groups
-//   = 256 threads, TT = TG*MT tokens per block, KC features per LDS stage.
+//   = 256 threads, TT = TG*MT tokens per block, at most KC features per LDS
+//   stage (a stage holds KC features when KC divides d, else 64; d is a
+//   multiple of 64).
 template <int EP>
 struct RouteShape;
 #define ROUTE_SHAPE(EP_, ME_, MT_, KC_)                        \
@@ -70,12 +72,14 @@ struct RouteShape;
     static constexpr int TT = (256 / (EP_ / ME_)) * MT_;       \
   };
 // Few tokens per block (16-128) so that even the smaller layers spread over
-// every CU; at 256 experts the stage is 16 features so that two blocks fit
+// every CU. With few experts the block is 32 tokens and a stage is up to 128
+// features: the loop over d then has few stages, each of which waits for its
+// loads once. At 256 experts the stage is 16 features so that two blocks fit
 // in one CU's LDS.
-ROUTE_SHAPE(8, 4, 1, 32)
-ROUTE_SHAPE(16, 4, 1, 32)
-ROUTE_SHAPE(32, 4, 2, 32)
-ROUTE_SHAPE(64, 8, 2, 32)
+ROUTE_SHAPE(8, 1, 1, 128)
+ROUTE_SHAPE(16, 2, 1, 128)
+ROUTE_SHAPE(32, 4, 1, 128)
+ROUTE_SHAPE(64, 8, 1, 64)
 ROUTE_SHAPE(128, 8, 4, 32)
 ROUTE_SHAPE(256, 8, 8, 16)
 ROUTE_SHAPE(512, 16, 4, 16)
@@ -85,7 +89,12 @@ ROUTE_SHAPE(1024, 16, 4, 8)
 template <int EP>
 struct RouteLds {
   using S = RouteShape<EP>;
-  static constexpr int kStage = 2 * S::KC * (S::TT + EP);  // floats
+  // One token per thread (MT = 1): stage rows are token- and expert-major,
+  // padded by 4 floats, so that a lane reads 4 features with one 16-byte
+  // load. Otherwise feature-major ([feature][token] and [feature][expert]).
+  static constexpr bool kRows = S::MT == 1;
+  static constexpr int kPitch = kRows ? S::KC + 4 : S::KC;
+  static constexpr int kStage = 2 * kPitch * (S::TT + EP);  // floats
   static constexpr int kLogits = S::TT * (EP + 1);          // floats
   static constexpr int kUnion = kStage > kLogits ? kStage : kLogits;
   static constexpr int kWords = (S::TT + 63) / 64;
@@ -151,6 +160,10 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   using S = RouteShape<EP>;
   using L = RouteLds<EP>;
   constexpr int ME = S::ME, MT = S::MT, KC = S::KC, EG = S::EG, TG = S::TG, TT = S::TT;
+  // features per register group of the gate-product loop (fewer when a
+  // thread holds many chains, to bound the registers)
+  constexpr int U = (ME * MT <= 4) ? 8 : ((ME * MT <= 16) ? 4 : 2);
+  static_assert(!RouteLds<EP>::kRows || U % 4 == 0, "row layout reads 4 features at a time");
   constexpr int V = XLoad<XT>::V;
   constexpr int W = L::kWords;
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -188,21 +201,25 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
 #pragma unroll
     for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
 
-  constexpr int XCH = TT * KC / V;             // 16-byte x loads per stage
-  constexpr int XPT = (XCH + 255) / 256;
-  constexpr int WCH = EP * KC / 4;             // 16-byte router-weight loads per stage
-  constexpr int WPT = (WCH + 255) / 256;
+  // features per stage: KC when it divides d, else 64 (d is a multiple of 64)
+  const int kc = (KC <= 64 || d % KC == 0) ? KC : 64;
+  const int xsh = __builtin_ctz((unsigned)(kc / V));  // log2 of 16-byte x loads per row and stage
+  const int wsh = __builtin_ctz((unsigned)(kc / 4));
+  const int XCH = TT * kc / V;                 // 16-byte x loads per stage
+  constexpr int XPT = (TT * KC / V + 255) / 256;
+  const int WCH = EP * kc / 4;                 // 16-byte router-weight loads per stage
+  constexpr int WPT = (EP * KC / 4 + 255) / 256;
   u32x4 xr[XPT], wreg[WPT];
-  const int nstage = d / KC;
+  const int nstage = d / kc;
 
   auto load_stage = [&](int s) {
-    const int k0 = s * KC;
+    const int k0 = s * kc;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int q = tid + i * 256;
       xr[i] = u32x4{0u, 0u, 0u, 0u};
       if (q < XCH) {
-        const int tt = q / (KC / V), c = q % (KC / V);
+        const int tt = q >> xsh, c = q & ((1 << xsh) - 1);
         if (tt < tt_count)
           xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * d + k0 + c * V);
       }
@@ -212,33 +229,95 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
       const int q = tid + i * 256;
       wreg[i] = u32x4{0u, 0u, 0u, 0u};
       if (q < WCH) {
-        const int e = q / (KC / 4), c = q % (KC / 4);
+        const int e = q >> wsh, c = q & ((1 << wsh) - 1);
         if (e < E) wreg[i] = *reinterpret_cast<const u32x4*>(wr + (size_t)e * d + k0 + c * 4);
       }
     }
   };
+  constexpr bool ROWS = L::kRows;
+  constexpr int PK = L::kPitch;
   auto store_stage = [&](int buf) {
-    float* xs = uni + buf * KC * (TT + EP);
-    float* ws = xs + KC * TT;
+    float* xs = uni + buf * PK * (TT + EP);
+    float* ws = xs + PK * TT;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int q = tid + i * 256;
       if (q < XCH) {
-        const int tt = q / (KC / V), c = q % (KC / V);
+        const int tt = q >> xsh, c = q & ((1 << xsh) - 1);
         float f[V];
         XLoad<XT>::widen(xr[i], f);
+        if constexpr (ROWS) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) xs[(c * V + v) * TT + tt] = f[v];
+          for (int v = 0; v < V; v += 4)
+            *reinterpret_cast<f32x4*>(xs + tt * PK + c * V + v) = f32x4{f[v], f[v + 1], f[v + 2], f[v + 3]};
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) xs[(c * V + v) * TT + tt] = f[v];
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int q = tid + i * 256;
       if (q < WCH) {
-        const int e = q / (KC / 4), c = q % (KC / 4);
+        const int e = q >> wsh, c = q & ((1 << wsh) - 1);
+        if constexpr (ROWS) {
+          *reinterpret_cast<u32x4*>(ws + e * PK + c * 4) = wreg[i];
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) ws[(c * 4 + v) * EP + e] = __uint_as_float(wreg[i][v]);
+          for (int v = 0; v < 4; ++v) ws[(c * 4 + v) * EP + e] = __uint_as_float(wreg[i][v]);
+        }
       }
+    }
+  };
+
+  auto compute_stage = [&](int s) {
+    const float* xs = uni + (s & 1) * PK * (TT + EP);
+    const float* ws = xs + PK * TT;
+    // Features in groups of U: the LDS reads of group g+1 are in flight while
+    // the fmas of group g run (every chain still adds its features in
+    // ascending order). kc is a multiple of 8, so of U.
+    float a[2][U][MT], b[2][U][ME];
+    auto read_group = [&](int h, int k0) {
+      if constexpr (ROWS) {
+#pragma unroll
+        for (int u = 0; u < U; u += 4) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(xs + tg * PK + k0 + u);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[h][u + q][0] = av[q];
+#pragma unroll
+          for (int j = 0; j < ME; ++j) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(ws + (eg * ME + j) * PK + k0 + u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b[h][u + q][j] = bv[q];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) a[h][u][i] = xs[(k0 + u) * TT + tg * MT + i];
+#pragma unroll
+          for (int j = 0; j < ME; ++j) b[h][u][j] = ws[(k0 + u) * EP + eg * ME + j];
+        }
+      }
+    };
+    auto fma_group = [&](int h) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < ME; ++j) acc[i][j] = __builtin_fmaf(a[h][u][i], b[h][u][j], acc[i][j]);
+    };
+    read_group(0, 0);
+#pragma unroll 1
+    for (int k0 = 0; k0 < kc; k0 += 2 * U) {
+      if (k0 + U < kc) read_group(1, k0 + U);
+      fma_group(0);
+      if (k0 + U >= kc) break;
+      if (k0 + 2 * U < kc) read_group(0, k0 + 2 * U);
+      fma_group(1);
     }
   };
 
@@ -247,20 +326,7 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   __syncthreads();
   for (int s = 0; s < nstage; ++s) {
     if (s + 1 < nstage) load_stage(s + 1);
-    const float* xs = uni + (s & 1) * KC * (TT + EP);
-    const float* ws = xs + KC * TT;
-#pragma unroll 4
-    for (int kk = 0; kk < KC; ++kk) {
-      float a[MT], b[ME];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) a[i] = xs[kk * TT + tg * MT + i];
-#pragma unroll
-      for (int j = 0; j < ME; ++j) b[j] = ws[kk * EP + eg * ME + j];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < ME; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-    }
+    compute_stage(s);
     if (s + 1 < nstage) store_stage((s + 1) & 1);
     __syncthreads();
   }
@@ -610,7 +676,7 @@ hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   using S = RouteShape<EP>;
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
-  if (a.d % S::KC || a.d % kLogKC) return hipErrorInvalidValue;
+  if (a.d % 64 || a.d % kLogKC) return hipErrorInvalidValue;  // stages of min(KC, 64) features
   // Split path when whole-row blocks would leave CUs idle and the experts are
   // many: logits first (grid over tokens and experts), then the selection.
   const bool split = a.logits != nullptr && a.E >= 64 && 4 * nb < cu_count_route();
