@@ -63,21 +63,34 @@ def traffic_from_profile(kernel: str, workload: str):
         return None
 
 
+def shared_as_group(cfg) -> bool:
+    """The library runs the shared expert as one more group of the routed
+    grouped GEMMs when it has the routed width and T * d_ff <= 2^25."""
+    return cfg.d_ff_s > 0 and cfg.d_ff_s == cfg.d_ff and cfg.T * cfg.d_ff_s <= 1 << 25
+
+
 def phase_bytes_and_flops(cfg):
     """Algorithmic work per phase (activated experts only)."""
     T, d, E, k, f, fs = cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff, cfg.d_ff_s
     b = 2 if cfg.dtype == "bf16" else 4
     rows = T * k
-    return {
+    work = {
         # x, W_r in; ids, weights, ranks out
         "route": {"bytes": T * d * b + E * d * 4 + rows * 12, "flops": 2.0 * T * d * E},
         "gateup": {"flops": 4.0 * rows * d * f, "bytes": rows * d * b + E * 2 * f * d * b + rows * f * b},
         "down": {"flops": 2.0 * rows * f * d, "bytes": rows * f * b + E * d * f * b + rows * d * 4},
-        "shared_gateup": {"flops": 4.0 * T * d * fs},
-        "shared_down": {"flops": 2.0 * T * fs * d},
+        "shared_gateup": {"flops": 4.0 * T * d * fs, "bytes": T * d * b + 2 * fs * d * b + T * fs * b},
+        "shared_down": {"flops": 2.0 * T * fs * d, "bytes": T * fs * b + d * fs * b + T * d * 4},
         # Y rows, weights and ids, shared rows in; y out
         "combine": {"bytes": rows * d * 4 + rows * 8 + (T * d * 4 if fs else 0) + T * d * 4},
     }
+    if shared_as_group(cfg):
+        # one gate/up and one down launch cover the routed and the shared expert
+        for a, s in (("gateup", "shared_gateup"), ("down", "shared_down")):
+            for key in ("flops", "bytes"):
+                work[a][key] += work[s][key]
+            del work[s]
+    return work
 
 
 def cpu_baseline(cfg, inputs, target_s: float):
@@ -150,7 +163,8 @@ def main():
     peak = PEAK_TFLOPS[cfg.dtype]
     gu = work["gateup"]["flops"] / (phase_ms["gateup"] * 1e-3) / 1e12
     traffic = traffic_from_profile("gateup", args.workload)
-    roofline = {"bound": "mfma", "kernel": "k_gemm<bf16, gate/up, grouped> (routed experts)",
+    what = "routed experts + the shared expert as one more group" if shared_as_group(cfg) else "routed experts"
+    roofline = {"bound": "mfma", "kernel": f"k_gemm<{cfg.dtype}, gate/up, grouped> ({what})",
                 "achieved": round(gu, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
     detail = {}
@@ -189,8 +203,7 @@ def main():
         "roofline": roofline,
         "phases": detail,
         "grouped_gemm_frac_mfma": round(
-            (work["gateup"]["flops"] + work["down"]["flops"] + work["shared_gateup"]["flops"]
-             + work["shared_down"]["flops"])
+            sum(work[n]["flops"] for n in ("gateup", "down", "shared_gateup", "shared_down") if n in work)
             / ((phase_ms["gateup"] + phase_ms["down"] + phase_ms["shared_gateup"] + phase_ms["shared_down"]) * 1e-3)
             / 1e12 / peak, 4),
     }

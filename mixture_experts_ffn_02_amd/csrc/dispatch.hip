@@ -15,23 +15,34 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
-// Exclusive prefix sum over v[0..n) in LDS (n <= kScanThreads), Hillis-Steele
-// on a scratch array; returns the total.
+// Exclusive prefix sum over v[0..n) in LDS (n <= kScanThreads): an inclusive
+// scan inside each wave with lane shuffles, then the scan of the wave totals
+// by wave 0; tmp holds at least kScanThreads / 64 ints. Returns the total.
 __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
-  const int tid = threadIdx.x;
-  int x = tid < n ? v[tid] : 0;
-  tmp[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int y = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += y;
-    __syncthreads();
+  constexpr int kWaves = kScanThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int x = tid < n ? v[tid] : 0;
+  int s = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(s, off);
+    if (lane >= off) s += y;
   }
-  const int incl = tmp[tid];
-  const int total = tmp[kScanThreads - 1];
+  if (lane == 63) tmp[w] = s;
   __syncthreads();
-  if (tid < n) v[tid] = incl - x;
+  if (w == 0) {
+    int t = lane < kWaves ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < kWaves) tmp[lane] = t;
+  }
+  __syncthreads();
+  const int before = w > 0 ? tmp[w - 1] : 0;
+  const int total = tmp[kWaves - 1];
+  if (tid < n) v[tid] = before + s - x;
   __syncthreads();
   return total;
 }
@@ -59,15 +70,18 @@ __global__ __launch_bounds__(kScanThreads) void k_counts(const int32_t* __restri
   }
 }
 
-// One block. Thread (g, e) owns expert e over block range g.
+// One block. Thread (g, e) owns expert e over block range g. `extra` > 0
+// appends one more group of that many rows after the E experts (offsets then
+// has E + 2 entries and the tile list ends with its tiles).
 __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict__ hist, int nb, int E,
                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ base, int bm,
-                                                       int32_t* __restrict__ n_tiles, int2* __restrict__ tiles) {
+                                                       int32_t* __restrict__ n_tiles, int2* __restrict__ tiles,
+                                                       int extra) {
   __shared__ int part[kScanThreads];
   __shared__ int cnt[kScanThreads];
   __shared__ int toff[kScanThreads];
-  __shared__ int tmp[kScanThreads];
+  __shared__ int tmp[kScanThreads / 64];
   const int tid = threadIdx.x;
   int ep = 1;
   while (ep < E) ep <<= 1;
@@ -80,31 +94,31 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
     for (int b = b0; b < b1; ++b) s += hist[(size_t)b * E + e];
   part[tid] = s;
   __syncthreads();
-  // per expert: exclusive prefix over the block ranges
-  if (g == 0 && e < E) {
-    int run = 0;
-    for (int gg = 0; gg < R; ++gg) {
-      const int v = part[gg * ep + e];
-      part[gg * ep + e] = run;
-      run += v;
-    }
-    cnt[e] = run;
+  // per expert: inclusive prefix over the block ranges, log2(R) steps
+  for (int off = 1; off < R; off <<= 1) {
+    const int y = g >= off ? part[tid - off * ep] : 0;
+    __syncthreads();
+    part[tid] += y;
+    __syncthreads();
   }
+  if (g == R - 1 && e < E) cnt[e] = part[tid];
   __syncthreads();
   if (tid < E) {
     counts[tid] = cnt[tid];
     toff[tid] = (cnt[tid] + bm - 1) / bm;
   }
   __syncthreads();
-  const int total = block_exclusive_scan(cnt, tmp, E);      // cnt -> offsets
+  const int total = block_exclusive_scan(cnt, tmp, E);  // cnt -> offsets
   const int total_tiles = block_exclusive_scan(toff, tmp, E);
+  const int extra_tiles = (extra + bm - 1) / bm;
   if (tid < E) offsets[tid] = cnt[tid];
   if (tid == 0) {
     offsets[E] = total;
-    n_tiles[0] = total_tiles;
+    if (extra > 0) offsets[E + 1] = total + extra;
+    n_tiles[0] = total_tiles + extra_tiles;
   }
   if (e < E) {
-    int run = cnt[e] + part[g * ep + e];
+    int run = cnt[e] + part[tid] - s;  // rows of expert e before block b0
     for (int b = b0; b < b1; ++b) {
       base[(size_t)b * E + e] = run;
       run += hist[(size_t)b * E + e];
@@ -114,13 +128,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
     const int nt = (tid + 1 < E ? toff[tid + 1] : total_tiles) - toff[tid];
     for (int i = 0; i < nt; ++i) tiles[toff[tid] + i] = make_int2(tid, i);
   }
+  for (int i = tid; i < extra_tiles; i += kScanThreads) tiles[total_tiles + i] = make_int2(E, i);
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_tiles_from_offsets(const int32_t* __restrict__ offsets, int G,
                                                                      int bm, int32_t* __restrict__ n_tiles,
                                                                      int2* __restrict__ tiles) {
   __shared__ int toff[kScanThreads];
-  __shared__ int tmp[kScanThreads];
+  __shared__ int tmp[kScanThreads / 64];
   const int tid = threadIdx.x;
   // groups are processed in slices of kScanThreads
   int carry = 0;
@@ -150,11 +165,12 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
                                                  const int32_t* __restrict__ base, int64_t T, int k, int E, int tpb,
                                                  int32_t* __restrict__ row_of, int32_t* __restrict__ tok_of_row,
                                                  const unsigned char* __restrict__ x, unsigned char* __restrict__ x_perm,
-                                                 int row_bytes) {
+                                                 int row_bytes, int extra) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int64_t n_rows = T * k;
+  if (extra && lane == 63) tok_of_row[n_rows + t] = (int32_t)t;  // the extra group: every token once
   int my_row = -1;
   if (lane < k) {
     const int e = idx[t * k + lane];
@@ -188,10 +204,10 @@ hipError_t launch_counts(const int32_t* hist, int nb, int E, int32_t* counts, hi
 }
 
 hipError_t launch_scan(const int32_t* hist, int nb, int E, int32_t* counts, int32_t* offsets, int32_t* base, int bm,
-                       int32_t* n_tiles, int2* tiles, hipStream_t s) {
-  if (E > kScanThreads) return hipErrorInvalidValue;
+                       int32_t* n_tiles, int2* tiles, hipStream_t s, int64_t extra) {
+  if (E > kScanThreads || extra < 0 || extra > 0x3FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, hist, nb, E, counts, offsets, base, bm, n_tiles,
-                     tiles);
+                     tiles, (int)extra);
   return hipGetLastError();
 }
 
@@ -203,11 +219,11 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int G, int bm, int3
 
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* base, int64_t T, int k, int E,
                           int tokens_per_block, int32_t* row_of, int32_t* tok_of_row, const void* x, void* x_perm,
-                          int row_bytes, hipStream_t s) {
+                          int row_bytes, hipStream_t s, bool extra) {
   if (T <= 0) return hipSuccess;
   const int64_t nb = (T + 3) / 4;
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)nb), dim3(256), 0, s, idx, rank, base, T, k, E, tokens_per_block,
-                     row_of, tok_of_row, (const unsigned char*)x, (unsigned char*)x_perm, row_bytes);
+                     row_of, tok_of_row, (const unsigned char*)x, (unsigned char*)x_perm, row_bytes, (int)extra);
   return hipGetLastError();
 }
 

@@ -200,8 +200,12 @@ void k_gemm(GemmLaunch g) {
     if (skip || rows <= 0) continue;  // uniform across the block
     const int n0 = tile_n * BN;
     const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
-    const unsigned char* B0 = reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
-    const unsigned char* B1 = GATEUP ? reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes : B0;
+    const bool xg = grp == g.extra_group;
+    const unsigned char* B0 = xg ? reinterpret_cast<const unsigned char*>(g.bx0)
+                                 : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
+    const unsigned char* B1 = !GATEUP ? B0
+                              : xg    ? reinterpret_cast<const unsigned char*>(g.bx1)
+                                      : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes;
 
     // Source row of each A run of this lane. Rows past the tile's end read a
     // valid row; their results are never stored. Weight rows are addressed

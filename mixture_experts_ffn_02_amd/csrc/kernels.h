@@ -42,15 +42,17 @@ hipError_t launch_hist_rank(const int32_t* idx, int64_t T, int k, int E, int32_t
 hipError_t launch_counts(const int32_t* hist, int nb, int E, int32_t* counts, hipStream_t s);
 // counts, offsets [E+1], per-block bases [nb, E], and the tile list of a
 // grouped GEMM with row tile bm: tiles[i] = (group, m-tile), n_tiles[0] = count.
+// extra > 0 appends group E of `extra` rows (offsets then has E + 2 entries).
 hipError_t launch_scan(const int32_t* hist, int nb, int E, int32_t* counts, int32_t* offsets, int32_t* base, int bm,
-                       int32_t* n_tiles, int2* tiles, hipStream_t s);
+                       int32_t* n_tiles, int2* tiles, hipStream_t s, int64_t extra = 0);
 // Tile list from device offsets [G+1].
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int G, int bm, int32_t* n_tiles, int2* tiles,
                                      hipStream_t s);
-// row_of [T, k], tok_of_row [T*k] and optionally x_perm rows.
+// row_of [T, k], tok_of_row [T*k] and optionally x_perm rows; with `extra`
+// also tok_of_row[T*k + t] = t (the rows of an appended all-token group).
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* base, int64_t T, int k, int E,
                           int tokens_per_block, int32_t* row_of, int32_t* tok_of_row, const void* x, void* x_perm,
-                          int row_bytes, hipStream_t s);
+                          int row_bytes, hipStream_t s, bool extra = false);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ------------------------------------------------------------------- GEMM
@@ -63,6 +65,9 @@ struct GemmLaunch {
   int n_groups;            // G (tile entries naming another group are skipped)
   const void* b0;          // [G, N, K]
   const void* b1;          // [G, N, K] (gateup)
+  int extra_group = -1;    // group whose weights are bx0 / bx1 instead of rows of b0 / b1 (-1: none)
+  const void* bx0 = nullptr;  // [N, K]
+  const void* bx1 = nullptr;  // [N, K] (gateup)
   void* out;               // [rows, N]
   int N, K;
   // grouped mode: tile list from launch_scan / launch_tiles_from_offsets

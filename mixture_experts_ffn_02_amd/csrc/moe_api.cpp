@@ -43,10 +43,21 @@ moe_status check_layer(const moe_layer* L, bool need_experts) {
   return MOE_OK;
 }
 
+// The shared expert joins the routed grouped GEMMs as one more group (all T
+// tokens, weight 1) when it has the routed width and is small (T * d_ff up to
+// 2^25): its own launches would leave the GPU partly idle, one gate/up and
+// one down launch over every expert do not. A large shared expert keeps two
+// dense launches, whose tiles (and weight traffic) spread over all XCDs; as
+// the last group of the tile list its tiles would fall to one XCD.
+bool shared_as_group(const moe_layer* L, int64_t T) {
+  return L->d_ff_shared > 0 && L->d_ff_shared == L->d_ff && T * (int64_t)L->d_ff_shared <= (int64_t)1 << 25;
+}
+
 struct Layout {
   size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row, idx, w, logits, mpart, h, yperm, hs,
       ys, total;
   int64_t nb;         // histogram rows (blocks)
+  int64_t gemm_rows;  // rows of the grouped GEMMs: T*k routed (+ T shared when it is a group)
   int64_t max_tiles;  // bound on grouped GEMM row tiles
 };
 
@@ -59,7 +70,9 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   const int64_t tpb_r = route_tokens_per_block((int)E), tpb_h = hist_tokens_per_block();
   const int64_t tpb = tpb_r < tpb_h ? tpb_r : tpb_h;
   o.nb = (T + tpb - 1) / tpb;
-  o.max_tiles = (rows + 127) / 128 + E;  // bound for the smallest row tile
+  const bool merged = shared_as_group(L, T);
+  o.gemm_rows = rows + (merged ? T : 0);
+  o.max_tiles = (o.gemm_rows + 127) / 128 + E + 1;  // bound for the smallest row tile
   size_t p = 0;
   auto take = [&](size_t bytes) {
     const size_t at = p;
@@ -70,19 +83,19 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   o.base = take(sizeof(int32_t) * (size_t)(o.nb * E));
   o.rank = take(sizeof(int32_t) * (size_t)rows);
   o.counts = take(sizeof(int32_t) * (size_t)E);
-  o.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+  o.offsets = take(sizeof(int32_t) * (size_t)(E + 2));
   o.n_tiles = take(sizeof(int32_t));
   o.tiles = take(sizeof(int2) * (size_t)o.max_tiles);
   o.row_of = take(sizeof(int32_t) * (size_t)rows);
-  o.tok_of_row = take(sizeof(int32_t) * (size_t)rows);
+  o.tok_of_row = take(sizeof(int32_t) * (size_t)o.gemm_rows);
   o.idx = take(sizeof(int32_t) * (size_t)rows);
   o.w = take(sizeof(float) * (size_t)rows);
   o.logits = take(sizeof(float) * (size_t)(T * E));
   o.mpart = take(sizeof(double) * (size_t)(o.nb * (E + 1)));
-  o.h = take((size_t)eb * (size_t)(rows * f));
-  o.yperm = take(sizeof(float) * (size_t)(rows * d));
-  o.hs = take((size_t)eb * (size_t)(T * fs));
-  o.ys = take(sizeof(float) * (size_t)(fs > 0 ? T * d : 0));
+  o.h = take((size_t)eb * (size_t)(o.gemm_rows * f));
+  o.yperm = take(sizeof(float) * (size_t)(o.gemm_rows * d));
+  o.hs = take((size_t)eb * (size_t)(merged ? 0 : T * fs));
+  o.ys = take(sizeof(float) * (size_t)(fs > 0 && !merged ? T * d : 0));
   o.total = p;
   return o;
 }
@@ -165,7 +178,10 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   int2* tiles = at<int2>(ws, lo.tiles);
   int32_t* row_of = at<int32_t>(ws, lo.row_of);
   int32_t* tok_of_row = at<int32_t>(ws, lo.tok_of_row);
-  const int bm = gemm_bm(L->dtype, (int64_t)T * k, E, L->d_ff);
+  const bool merged = shared_as_group(L, T);
+  if (merged && T * (int64_t)(k + 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
+  const int n_groups = E + (merged ? 1 : 0);
+  const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff);
   const int tpb = route_tokens_per_block(E);
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
@@ -173,10 +189,10 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   const RouteLaunch r = route_launch(L, x, T, opts, idx_p, w_p, hist, rank, ws, lo);
   MOE_TRY(launch_route(r, s));
   mark(tm, MOE_PHASE_SCAN, s);
-  MOE_TRY(launch_scan(hist, (int)nb_route, E, counts_p, offsets, base, bm, n_tiles, tiles, s));
+  MOE_TRY(launch_scan(hist, (int)nb_route, E, counts_p, offsets, base, bm, n_tiles, tiles, s, merged ? T : 0));
   if (r.mpart) MOE_TRY(launch_router_metrics(r.mpart, (int)nb_route, counts_p, T, E, k, opts->metrics, s));
   mark(tm, MOE_PHASE_SCATTER, s);
-  MOE_TRY(launch_scatter(idx_p, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s));
+  MOE_TRY(launch_scatter(idx_p, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s, merged));
 
   mark(tm, MOE_PHASE_GATEUP, s);
   GemmLaunch gu{};
@@ -185,9 +201,14 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   gu.a = x;
   gu.a_rows = tok_of_row;
   gu.a_row_count = T;
-  gu.n_groups = E;
+  gu.n_groups = n_groups;
   gu.b0 = L->w_gate;
   gu.b1 = L->w_up;
+  if (merged) {
+    gu.extra_group = E;
+    gu.bx0 = L->ws_gate;
+    gu.bx1 = L->ws_up;
+  }
   gu.out = at<void>(ws, lo.h);
   gu.N = L->d_ff;
   gu.K = d;
@@ -203,15 +224,18 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   dn.a_rows = nullptr;
   dn.b0 = L->w_down;
   dn.b1 = nullptr;
+  dn.bx0 = L->ws_down;
+  dn.bx1 = nullptr;
   dn.out = at<void>(ws, lo.yperm);
   dn.N = d;
   dn.K = L->d_ff;
   MOE_TRY(launch_gemm(dn, bm, s));
 
-  const float* shared_out = nullptr;
+  // shared expert: rows T*k .. T*k+T-1 of the grouped output, or its own GEMMs
+  const float* shared_out = merged ? at<float>(ws, lo.yperm) + (size_t)T * k * d : nullptr;
   const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared);
   mark(tm, MOE_PHASE_SHARED_GATEUP, s);
-  if (L->d_ff_shared > 0) {
+  if (L->d_ff_shared > 0 && !merged) {
     GemmLaunch sg{};
     sg.dtype = L->dtype;
     sg.gateup = true;
@@ -225,7 +249,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     MOE_TRY(launch_gemm(sg, bm_s, s));
   }
   mark(tm, MOE_PHASE_SHARED_DOWN, s);
-  if (L->d_ff_shared > 0) {
+  if (L->d_ff_shared > 0 && !merged) {
     GemmLaunch sd{};
     sd.dtype = L->dtype;
     sd.gateup = false;
