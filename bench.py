@@ -79,8 +79,8 @@ def phase_bytes_and_flops(cfg):
         "route": {"bytes": T * d * b + E * d * 4 + rows * 12, "flops": 2.0 * T * d * E},
         "gateup": {"flops": 4.0 * rows * d * f, "bytes": rows * d * b + E * 2 * f * d * b + rows * f * b},
         "down": {"flops": 2.0 * rows * f * d, "bytes": rows * f * b + E * d * f * b + rows * d * 4},
-        "shared_gateup": {"flops": 4.0 * T * d * fs, "bytes": T * d * b + 2 * fs * d * b + T * fs * b},
-        "shared_down": {"flops": 2.0 * T * fs * d, "bytes": T * fs * b + d * fs * b + T * d * 4},
+        "shared_gateup": {"flops": 4.0 * T * d * fs, "bytes": (T * d * b + 2 * fs * d * b + T * fs * b) if fs else 0},
+        "shared_down": {"flops": 2.0 * T * fs * d, "bytes": (T * fs * b + d * fs * b + T * d * 4) if fs else 0},
         # Y rows, weights and ids, shared rows in; y out
         "combine": {"bytes": rows * d * 4 + rows * 8 + (T * d * 4 if fs else 0) + T * d * 4},
     }
@@ -177,7 +177,7 @@ def main():
             tf = w["flops"] / t_s / 1e12
             pk = PEAK_VALU_F32_TFLOPS if name == "route" else peak
             e.update(tflops=round(tf, 2), frac_compute_peak=round(tf / pk, 4))
-        if "bytes" in w:
+        if w.get("bytes"):
             gbs = w["bytes"] / t_s / 1e9
             e.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
         detail[name] = e

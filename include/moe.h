@@ -256,7 +256,9 @@ moe_status moe_forward_ex(const moe_layer *layer, const void *x, int64_t T, cons
 #define MOE_PHASE_COMBINE 7        /* weighted combine */
 #define MOE_N_PHASES 8
 
-/* Create / destroy a timing record (creates hipEvents on the current device). */
+/* Create / destroy a timing record (creates hipEvents on the current device,
+ * without a system-scope fence, so recording them does not flush caches
+ * between the phases they time). */
 moe_status moe_timing_create(moe_timing **out);
 moe_status moe_timing_destroy(moe_timing *t);
 

@@ -453,7 +453,9 @@ moe_status moe_timing_create(moe_timing** out) {
   moe_timing* t = new (std::nothrow) moe_timing;
   if (!t) return MOE_ERR_HIP;
   for (int i = 0; i <= MOE_N_PHASES; ++i) {
-    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+    // timing-only events: no system-scope fence (no cache writeback and
+    // invalidation between the phases they separate)
+    if (hipEventCreateWithFlags(&t->ev[i], hipEventDisableSystemFence) != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
       delete t;
       return MOE_ERR_HIP;
