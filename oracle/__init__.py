@@ -54,6 +54,9 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_route_ex.argtypes = [i32, vp, i64, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.oracle_router_metrics.argtypes = [vp, vp, i64, i32, i32, i32, vp]
     lib.oracle_bias_update.argtypes = [vp, i32, ctypes.c_float, vp]
+    lib.oracle_backward.restype = i32
+    lib.oracle_backward.argtypes = [i32, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                    vp, vp, vp, ctypes.c_double, ctypes.c_double] + [vp] * 9
     lib.oracle_dispatch.restype = i32
     lib.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp]
     lib.oracle_experts.restype = i32
@@ -220,4 +223,38 @@ def forward(inputs: Dict[str, np.ndarray], top_k: int, score: str, renorm: bool 
                 inputs.get("ws_gate"), inputs.get("ws_up"), inputs.get("ws_down"), L=L)
     out = dict(r)
     out.update(offsets=dsp["offsets"], row_of=dsp["row_of"], y=y, tokens=np.asarray(tokens, np.int64))
+    return out
+
+
+def backward(inputs: Dict[str, np.ndarray], idx, w, dy, score: str, renorm: bool = True, z_coef: float = 0.0,
+             aux_coef: float = 0.0, L=None) -> Dict[str, np.ndarray]:
+    """fp64 gradients of the layer for a given routing (idx, w from the forward
+    pass) and output gradient dy [T, d]: dx, dw_router, dw_gate, dw_up,
+    dw_down, the shared expert's (or None) and d_topk_w (the combine weights)."""
+    x = _c(inputs["x"])
+    T, d = x.shape
+    wr = _c(inputs["w_router"], np.float32)
+    wg, wu, wd = _c(inputs["w_gate"]), _c(inputs["w_up"]), _c(inputs["w_down"])
+    E, d_ff, _ = wg.shape
+    sg, su, sd = _c(inputs.get("ws_gate")), _c(inputs.get("ws_up")), _c(inputs.get("ws_down"))
+    d_ff_s = 0 if sg is None else sg.shape[0]
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    dy = _c(dy, np.float32)
+    k = idx.shape[1]
+    out = {
+        "dx": np.zeros((T, d)), "dw_router": np.zeros((E, d)), "dw_gate": np.zeros((E, d_ff, d)),
+        "dw_up": np.zeros((E, d_ff, d)), "dw_down": np.zeros((E, d, d_ff)),
+        "dws_gate": None if sg is None else np.zeros((d_ff_s, d)),
+        "dws_up": None if sg is None else np.zeros((d_ff_s, d)),
+        "dws_down": None if sg is None else np.zeros((d, d_ff_s)),
+        "d_topk_w": np.zeros((T, k)),
+    }
+    rc = (L or lib()).oracle_backward(
+        _dt(x), _p(x), T, d, E, k, d_ff, d_ff_s, _p(wr), _p(wg), _p(wu), _p(wd), _p(sg), _p(su), _p(sd),
+        SCORE[score], int(bool(renorm)), _p(idx), _p(w), _p(dy), float(z_coef), float(aux_coef),
+        *[_p(out[n]) for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
+                               "d_topk_w")])
+    if rc != 0:
+        raise ValueError("oracle_backward: expert index out of range")
     return out

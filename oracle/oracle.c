@@ -643,3 +643,315 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------ */
+/* backward                                                                  */
+/* ------------------------------------------------------------------------ */
+
+static double sigm(double z)
+{
+    return 1.0 / (1.0 + exp(-z));
+}
+
+/* One SwiGLU expert on one token in fp64, keeping what its backward needs:
+ * g = W_gate a, u = W_up a, h = silu(g) u, out = W_down h. */
+static void expert_forward(int dtype, int d, int d_ff, const double *a, const void *wg, const void *wu,
+                           const void *wd, size_t off_gu, size_t off_d, double *g, double *u, double *h, double *out)
+{
+    int f, c;
+    for (f = 0; f < d_ff; f++) {
+        double sg = 0.0, su = 0.0;
+        for (c = 0; c < d; c++) {
+            sg += (double)elem(wg, dtype, off_gu + (size_t)f * d + c) * a[c];
+            su += (double)elem(wu, dtype, off_gu + (size_t)f * d + c) * a[c];
+        }
+        g[f] = sg;
+        u[f] = su;
+        h[f] = silu(sg) * su;
+    }
+    if (out)
+        for (c = 0; c < d; c++) {
+            double s = 0.0;
+            for (f = 0; f < d_ff; f++)
+                s += (double)elem(wd, dtype, off_d + (size_t)c * d_ff + f) * h[f];
+            out[c] = s;
+        }
+}
+
+/* Backward of that expert given dout, the gradient of its output:
+ * dh = W_down^T dout, dg = dh u silu'(g), du = dh silu(g), with
+ * silu'(z) = s (1 + z (1 - s)), s = sigmoid(z). */
+static void expert_backward(int dtype, int d, int d_ff, const void *wd, size_t off_d, const double *g,
+                            const double *u, const double *dout, double *dg, double *du)
+{
+    int f, c;
+    for (f = 0; f < d_ff; f++) {
+        double dh = 0.0, s = sigm(g[f]);
+        for (c = 0; c < d; c++)
+            dh += (double)elem(wd, dtype, off_d + (size_t)c * d_ff + f) * dout[c];
+        dg[f] = dh * u[f] * s * (1.0 + g[f] * (1.0 - s));
+        du[f] = dh * g[f] * s;
+    }
+}
+
+/* da += W_gate^T dg + W_up^T du */
+static void expert_input_grad(int dtype, int d, int d_ff, const void *wg, const void *wu, size_t off_gu,
+                              const double *dg, const double *du, double *da)
+{
+    int f, c;
+    for (f = 0; f < d_ff; f++)
+        for (c = 0; c < d; c++)
+            da[c] += (double)elem(wg, dtype, off_gu + (size_t)f * d + c) * dg[f] +
+                     (double)elem(wu, dtype, off_gu + (size_t)f * d + c) * du[f];
+}
+
+/*
+ * Gradient of the router logits of one token (fp64, from the fp32 logits l
+ * and the combine-weight gradients dtw of its k slots), for the weight rule
+ * of the forward pass (README "SigmoidRouter": weights gathered from the
+ * unbiased scores and renormalised; PR #930 "What this adds": softmax over
+ * all experts, top-k renormalised), plus the z-loss and aux-loss terms of
+ * "SigmoidRouter" scaled by their coefficients:
+ *   z_loss = mean_t lse_t^2                -> 2 lse_t softmax(l_t) / T
+ *   aux    = E sum_e f_e mean_t score_te,  f_e = counts_e / T (a constant)
+ * The selection itself (top-k, bias, noise) is piecewise constant and passes
+ * no gradient.
+ */
+static void router_token_grad(const float *l, int E, int k, const int32_t *idx, const double *dtw, int score,
+                              int renorm, int64_t T, const double *f, double z_coef, double aux_coef, double *dl)
+{
+    int e, j;
+    double m = l[0], z = 0.0, lse;
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    for (e = 1; e < E; e++)
+        if (l[e] > m)
+            m = l[e];
+    for (e = 0; e < E; e++)
+        z += exp((double)l[e] - m);
+    lse = m + log(z);
+    for (e = 0; e < E; e++) {
+        p[e] = exp((double)l[e] - m) / z;
+        dl[e] = 0.0;
+    }
+    if (score == SCORE_SOFTMAX && renorm) {
+        double mk = l[idx[0]], zk = 0.0, dot = 0.0;
+        for (j = 1; j < k; j++)
+            if (l[idx[j]] > mk)
+                mk = l[idx[j]];
+        for (j = 0; j < k; j++)
+            zk += exp((double)l[idx[j]] - mk);
+        for (j = 0; j < k; j++)
+            dot += exp((double)l[idx[j]] - mk) / zk * dtw[j];
+        for (j = 0; j < k; j++)
+            dl[idx[j]] += exp((double)l[idx[j]] - mk) / zk * (dtw[j] - dot);
+    } else if (score == SCORE_SOFTMAX) {
+        double dot = 0.0;
+        for (j = 0; j < k; j++)
+            dot += p[idx[j]] * dtw[j];
+        for (e = 0; e < E; e++)
+            dl[e] -= p[e] * dot;
+        for (j = 0; j < k; j++)
+            dl[idx[j]] += p[idx[j]] * dtw[j];
+    } else if (renorm) {
+        double S = 0.0, dot = 0.0, D;
+        for (j = 0; j < k; j++)
+            S += sigm(l[idx[j]]);
+        D = S + 1e-9;
+        for (j = 0; j < k; j++)
+            dot += dtw[j] * sigm(l[idx[j]]);
+        for (j = 0; j < k; j++) {
+            double s = sigm(l[idx[j]]);
+            dl[idx[j]] += (dtw[j] / D - dot / (D * D)) * s * (1.0 - s);
+        }
+    } else {
+        for (j = 0; j < k; j++) {
+            double s = sigm(l[idx[j]]);
+            dl[idx[j]] += dtw[j] * s * (1.0 - s);
+        }
+    }
+    if (z_coef != 0.0)
+        for (e = 0; e < E; e++)
+            dl[e] += z_coef * 2.0 * lse * p[e] / (double)T;
+    if (aux_coef != 0.0) {
+        double fp = 0.0;
+        for (e = 0; e < E; e++)
+            fp += f[e] * p[e];
+        for (e = 0; e < E; e++) {
+            if (score == SCORE_SIGMOID) {
+                double s = sigm(l[e]);
+                dl[e] += aux_coef * (double)E / (double)T * f[e] * s * (1.0 - s);
+            } else {
+                dl[e] += aux_coef * (double)E / (double)T * p[e] * (f[e] - fp);
+            }
+        }
+    }
+    free(p);
+}
+
+/*
+ * Backward pass of the layer for a given routing (idx, w from the forward
+ * pass) and output gradient dy [T, d] fp32, all in fp64 on the exact inputs:
+ *   d_topk_w[t, j] = <dy_t, E_e(x_t)>,        e = idx[t, j]
+ *   expert e, token t:  dout = w[t, j] dy_t;  dW_down[e] += dout h^T;
+ *     dW_gate[e] += dg x_t^T;  dW_up[e] += du x_t^T;  dx_t += W_gate^T dg + W_up^T du
+ *   shared expert: the same with dout = dy_t
+ *   router: dlogits from d_topk_w (router_token_grad); dW_router = dlogits^T x;
+ *     dx_t += W_router^T dlogits_t
+ * The logits are the forward's fp32 ones (oracle_logits). Weight gradients
+ * are summed over tokens in ascending order. The shared weights and their
+ * gradients may be NULL (no shared expert). Returns nonzero for an expert id
+ * out of range.
+ */
+int oracle_backward(int dtype, const void *x, int64_t T, int d, int E, int k, int d_ff, int d_ff_s,
+                    const float *w_router, const void *w_gate, const void *w_up, const void *w_down,
+                    const void *ws_gate, const void *ws_up, const void *ws_down, int score, int renorm,
+                    const int32_t *idx, const float *w, const float *dy, double z_coef, double aux_coef, double *dx,
+                    double *dw_router, double *dw_gate, double *dw_up, double *dw_down, double *dws_gate,
+                    double *dws_up, double *dws_down, double *d_topk_w)
+{
+    float *lg;
+    double *f, *dl;
+    int64_t t, n = T * k;
+    int e, bad = 0;
+    for (t = 0; t < n; t++)
+        if (idx[t] < 0 || idx[t] >= E)
+            return 1;
+    lg = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+    f = (double *)calloc((size_t)E, sizeof(double));
+    dl = (double *)calloc((size_t)(T > 0 ? T : 1) * (size_t)E, sizeof(double));
+    oracle_logits(dtype, x, T, d, w_router, E, lg);
+    for (t = 0; t < n; t++)
+        f[idx[t]] += 1.0 / (double)T;
+
+    /* per token: combine-weight gradients, router logit gradients, dx */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < T; t++) {
+        int c, j, ds = d_ff_s > 0 ? d_ff_s : 1;
+        int mf = d_ff > ds ? d_ff : ds;
+        double *a = (double *)malloc(sizeof(double) * (size_t)d);
+        double *g = (double *)malloc(sizeof(double) * (size_t)mf);
+        double *u = (double *)malloc(sizeof(double) * (size_t)mf);
+        double *h = (double *)malloc(sizeof(double) * (size_t)mf);
+        double *dg = (double *)malloc(sizeof(double) * (size_t)mf);
+        double *du = (double *)malloc(sizeof(double) * (size_t)mf);
+        double *out = (double *)malloc(sizeof(double) * (size_t)d);
+        double *dout = (double *)malloc(sizeof(double) * (size_t)d);
+        double *dtw = (double *)malloc(sizeof(double) * (size_t)k);
+        double *da = dx + (size_t)t * d;
+        for (c = 0; c < d; c++) {
+            a[c] = (double)elem(x, dtype, (size_t)t * d + c);
+            da[c] = 0.0;
+        }
+        for (j = 0; j < k; j++) {
+            int ee = idx[t * k + j];
+            size_t ogu = (size_t)ee * d_ff * d, od = (size_t)ee * d * d_ff;
+            double s = 0.0;
+            expert_forward(dtype, d, d_ff, a, w_gate, w_up, w_down, ogu, od, g, u, h, out);
+            for (c = 0; c < d; c++) {
+                s += (double)dy[(size_t)t * d + c] * out[c];
+                dout[c] = (double)w[t * k + j] * (double)dy[(size_t)t * d + c];
+            }
+            dtw[j] = s;
+            if (d_topk_w)
+                d_topk_w[t * k + j] = s;
+            expert_backward(dtype, d, d_ff, w_down, od, g, u, dout, dg, du);
+            expert_input_grad(dtype, d, d_ff, w_gate, w_up, ogu, dg, du, da);
+        }
+        if (ws_gate) {
+            for (c = 0; c < d; c++)
+                dout[c] = (double)dy[(size_t)t * d + c];
+            expert_forward(dtype, d, d_ff_s, a, ws_gate, ws_up, ws_down, 0, 0, g, u, h, NULL);
+            expert_backward(dtype, d, d_ff_s, ws_down, 0, g, u, dout, dg, du);
+            expert_input_grad(dtype, d, d_ff_s, ws_gate, ws_up, 0, dg, du, da);
+        }
+        router_token_grad(lg + (size_t)t * E, E, k, idx + t * k, dtw, score, renorm, T, f, z_coef, aux_coef,
+                          dl + (size_t)t * E);
+        for (j = 0; j < E; j++)
+            for (c = 0; c < d; c++)
+                da[c] += dl[(size_t)t * E + j] * (double)w_router[(size_t)j * d + c];
+        free(a);
+        free(g);
+        free(u);
+        free(h);
+        free(dg);
+        free(du);
+        free(out);
+        free(dout);
+        free(dtw);
+    }
+
+    /* weight gradients, one expert (or the shared expert, index E) at a time */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (e = 0; e <= E; e++) {
+        int shared = e == E, ff = shared ? d_ff_s : d_ff, c, j, q;
+        size_t ogu = shared ? 0 : (size_t)e * d_ff * d, od = shared ? 0 : (size_t)e * d * d_ff;
+        const void *wg = shared ? ws_gate : w_gate, *wu = shared ? ws_up : w_up, *wd = shared ? ws_down : w_down;
+        double *Gg = shared ? dws_gate : dw_gate + ogu, *Gu = shared ? dws_up : dw_up + ogu;
+        double *Gd = shared ? dws_down : dw_down + od;
+        double *a, *g, *u, *h, *dg, *du, *dout;
+        int64_t tt;
+        if (shared && !ws_gate)
+            continue;
+        a = (double *)malloc(sizeof(double) * (size_t)d);
+        g = (double *)malloc(sizeof(double) * (size_t)ff);
+        u = (double *)malloc(sizeof(double) * (size_t)ff);
+        h = (double *)malloc(sizeof(double) * (size_t)ff);
+        dg = (double *)malloc(sizeof(double) * (size_t)ff);
+        du = (double *)malloc(sizeof(double) * (size_t)ff);
+        dout = (double *)malloc(sizeof(double) * (size_t)d);
+        memset(Gg, 0, sizeof(double) * (size_t)ff * d);
+        memset(Gu, 0, sizeof(double) * (size_t)ff * d);
+        memset(Gd, 0, sizeof(double) * (size_t)d * ff);
+        for (tt = 0; tt < T; tt++) {
+            for (j = 0; j < (shared ? 1 : k); j++) {
+                double wt = 1.0;
+                if (!shared) {
+                    if (idx[tt * k + j] != e)
+                        continue;
+                    wt = (double)w[tt * k + j];
+                }
+                for (c = 0; c < d; c++) {
+                    a[c] = (double)elem(x, dtype, (size_t)tt * d + c);
+                    dout[c] = wt * (double)dy[(size_t)tt * d + c];
+                }
+                expert_forward(dtype, d, ff, a, wg, wu, wd, ogu, od, g, u, h, NULL);
+                expert_backward(dtype, d, ff, wd, od, g, u, dout, dg, du);
+                for (c = 0; c < d; c++)
+                    for (q = 0; q < ff; q++)
+                        Gd[(size_t)c * ff + q] += dout[c] * h[q];
+                for (q = 0; q < ff; q++)
+                    for (c = 0; c < d; c++) {
+                        Gg[(size_t)q * d + c] += dg[q] * a[c];
+                        Gu[(size_t)q * d + c] += du[q] * a[c];
+                    }
+            }
+        }
+        free(a);
+        free(g);
+        free(u);
+        free(h);
+        free(dg);
+        free(du);
+        free(dout);
+    }
+
+    /* router weight gradient: dW_router[e] = sum_t dlogits[t, e] x_t */
+#pragma omp parallel for
+    for (e = 0; e < E; e++) {
+        int c;
+        int64_t tt;
+        for (c = 0; c < d; c++)
+            dw_router[(size_t)e * d + c] = 0.0;
+        for (tt = 0; tt < T; tt++) {
+            double v = dl[(size_t)tt * E + e];
+            if (v == 0.0)
+                continue;
+            for (c = 0; c < d; c++)
+                dw_router[(size_t)e * d + c] += v * (double)elem(x, dtype, (size_t)tt * d + c);
+        }
+    }
+    free(lg);
+    free(f);
+    free(dl);
+    return bad;
+}

@@ -462,6 +462,82 @@ def check_bias_update(L) -> None:
     assert first > 1.0 and cv < 0.05, f"controller did not balance: cv {first:.3f} -> {cv:.3f}"
 
 
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def torch_layer_grads(inp, idx, dy, score, renorm, z_coef, aux_coef):
+    """Gradients of sum(y * dy) + z_coef z_loss + aux_coef aux_loss by torch
+    float64 autograd on the CPU, over a plain forward written with torch ops
+    for the given (fixed) expert choice (README "SigmoidRouter": weights from
+    the unbiased scores, z-loss, aux loss with one-hot counts as a constant)."""
+    import torch
+    import torch.nn.functional as F
+
+    def param(a):
+        return torch.tensor(widen(a), dtype=torch.float64, requires_grad=True)
+
+    x = param(inp["x"])
+    Wr = torch.tensor(inp["w_router"].astype(np.float64), requires_grad=True)
+    Wg, Wu, Wd = param(inp["w_gate"]), param(inp["w_up"]), param(inp["w_down"])
+    T, d = x.shape
+    E, k = Wr.shape[0], idx.shape[1]
+    it = torch.tensor(idx, dtype=torch.long)
+    logits = x @ Wr.T
+    sel = torch.gather(logits, 1, it)
+    if score == "softmax":
+        w = torch.softmax(sel, 1) if renorm else torch.gather(torch.softmax(logits, 1), 1, it)
+    else:
+        s = torch.sigmoid(sel)
+        w = s / (s.sum(1, keepdim=True) + 1e-9) if renorm else s
+    w.retain_grad()
+    y = torch.zeros((T, d), dtype=torch.float64)
+    for e in range(E):
+        tok, slot = (it == e).nonzero(as_tuple=True)
+        if tok.numel() == 0:
+            continue
+        a = x[tok]
+        out = (F.silu(a @ Wg[e].T) * (a @ Wu[e].T)) @ Wd[e].T
+        y = y.index_add(0, tok, w[tok, slot].unsqueeze(1) * out)
+    shared = inp.get("ws_gate") is not None
+    if shared:
+        Sg, Su, Sd = param(inp["ws_gate"]), param(inp["ws_up"]), param(inp["ws_down"])
+        y = y + (F.silu(x @ Sg.T) * (x @ Su.T)) @ Sd.T
+    loss = (y * torch.tensor(dy.astype(np.float64))).sum()
+    if z_coef:
+        loss = loss + z_coef * (torch.logsumexp(logits, 1) ** 2).mean()
+    if aux_coef:
+        f = torch.bincount(it.reshape(-1), minlength=E).to(torch.float64) / T
+        sc = torch.sigmoid(logits) if score == "sigmoid" else torch.softmax(logits, 1)
+        loss = loss + aux_coef * E * (f * sc.mean(0)).sum()
+    loss.backward()
+    g = {"dx": x.grad, "dw_router": Wr.grad, "dw_gate": Wg.grad, "dw_up": Wu.grad, "dw_down": Wd.grad,
+         "d_topk_w": w.grad}
+    if shared:
+        g.update(dws_gate=Sg.grad, dws_up=Su.grad, dws_down=Sd.grad)
+    return {n: v.numpy() for n, v in g.items()}
+
+
+def check_backward_autograd(L) -> None:
+    """The oracle's backward equals torch float64 autograd of the plain forward
+    (same expert choice) for both scores, with and without renormalisation, a
+    shared expert, bf16 and fp32 inputs, and nonzero z-loss and aux-loss
+    coefficients: every gradient within 1e-6 of its largest entry (the oracle
+    takes the forward's fp32 logits and weights, autograd fp64 ones)."""
+    cases = (("softmax", True, "bf16", True, 0.3, 0.2), ("softmax", False, "f32", False, 0.0, 0.0),
+             ("sigmoid", True, "bf16", True, 0.1, 0.5), ("sigmoid", False, "f32", True, 0.2, 0.0))
+    for score, renorm, dtype, shared, zc, ac in cases:
+        cfg, inp = small_layer(T=48, d=64, E=6, k=2, d_ff=64, dtype=dtype, score=score, shared=shared,
+                               bias_range=0.2, seed=21)
+        r = oracle.route(inp["x"], inp["w_router"], inp["sel_bias"], 2, score, renorm, L=L)
+        dy = np.random.default_rng(5).standard_normal((48, 64)).astype(np.float32)
+        got = oracle.backward(inp, r["idx"], r["w"], dy, score, renorm, zc, ac, L=L)
+        ref = torch_layer_grads(inp, r["idx"], dy, score, renorm, zc, ac)
+        for n, v in ref.items():
+            err = np.abs(got[n] - v).max() / max(np.abs(v).max(), 1e-30)
+            assert err < 1e-6, f"{score}/renorm={renorm}/{dtype}: {n} differs from autograd by {err:.2e}"
+
+
 ALL_CHECKS = [check_cexpf, check_logits, check_topk_bruteforce, check_topk_lexsort, check_weights,
               check_bias_selection_only, check_dispatch, check_dense_masked, check_dense_swiglu, check_envelope,
-              check_route_options, check_router_metrics, check_bias_update]
+              check_route_options, check_router_metrics, check_bias_update, check_backward_autograd]

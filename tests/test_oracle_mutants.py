@@ -39,6 +39,16 @@ MUTANTS = {
     "metrics_z_without_max": ("lse = m + log(s);", "lse = log(s);"),
     "logit_bias_dropped": ("            v[e] = l[e] + bias[e];\n", "            v[e] = l[e];\n"),
     "noise_dropped": ("v[e] = v[e] + noise[e];", "v[e] = v[e] + 0.0f;"),
+    "bwd_silu_prime_dropped": ("dg[f] = dh * u[f] * s * (1.0 + g[f] * (1.0 - s));", "dg[f] = dh * u[f] * s;"),
+    "bwd_du_from_u": ("du[f] = dh * g[f] * s;", "du[f] = dh * u[f] * s;"),
+    "bwd_softmax_jacobian_sign": ("dl[idx[j]] += exp((double)l[idx[j]] - mk) / zk * (dtw[j] - dot);",
+                                  "dl[idx[j]] += exp((double)l[idx[j]] - mk) / zk * (dtw[j] + dot);"),
+    "bwd_sigmoid_renorm_cross_term": ("dl[idx[j]] += (dtw[j] / D - dot / (D * D)) * s * (1.0 - s);",
+                                      "dl[idx[j]] += (dtw[j] / D) * s * (1.0 - s);"),
+    "bwd_zloss_factor": ("dl[e] += z_coef * 2.0 * lse * p[e] / (double)T;", "dl[e] += z_coef * lse * p[e] / (double)T;"),
+    "bwd_router_dx_dropped": ("da[c] += dl[(size_t)t * E + j] * (double)w_router[(size_t)j * d + c];",
+                              "da[c] += 0.0 * w_router[(size_t)j * d + c];"),
+    "bwd_weight_grad_unweighted": ("                    wt = (double)w[tt * k + j];", "                    wt = 1.0;"),
     "count_off_by_one": ("        counts[idx[t]]++;\n    if (!logits_out)",
                          "        counts[idx[t] == 0 ? 1 : idx[t]]++;\n    if (!logits_out)"),
 }
