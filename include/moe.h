@@ -242,6 +242,48 @@ moe_status moe_forward_ex(const moe_layer *layer, const void *x, int64_t T, cons
                           void *stream, moe_timing *timing);
 
 /* ---------------------------------------------------------------------- */
+/* Backward pass (training)                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Gradients written by moe_backward: fp32 DEVICE arrays owned by the caller. */
+typedef struct moe_grads {
+    float *dx;          /* [T, d] */
+    float *dw_router;   /* [E, d] */
+    float *dw_gate;     /* [E, d_ff, d] */
+    float *dw_up;       /* [E, d_ff, d] */
+    float *dw_down;     /* [E, d, d_ff] */
+    float *dws_gate;    /* [d_ff_shared, d], or NULL without a shared expert */
+    float *dws_up;      /* [d_ff_shared, d], or NULL */
+    float *dws_down;    /* [d, d_ff_shared], or NULL */
+    float *d_topk_w;    /* [T, k] gradient of the combine weights, or NULL */
+} moe_grads;
+
+/* Workspace bytes for moe_backward. */
+moe_status moe_backward_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
+
+/*
+ * Backward pass of the layer for the routing of its forward pass (README,
+ * "SigmoidRouter" and "Architecture diagram"; PR #930, "Tests"): given
+ * dy = dL/dy [T, d] fp32, writes dL/dx, the weight gradients and the
+ * combine-weight gradients, for
+ *   L' = L + z_loss_coef * z_loss + aux_loss_coef * aux_loss
+ * (the SigmoidRouter z-loss and aux loss, one-hot counts taken as constants;
+ * coefficients 0 leave them out). The expert choice passes no gradient; the
+ * router's gradient flows through the combine weights, computed from the
+ * unbiased scores as in the forward pass. The selection bias and any noise
+ * have no gradient.
+ *   x        [T, d] layer dtype (the forward's input)
+ *   topk_idx [T, k], topk_w [T, k]: the forward's outputs
+ * Activations are recomputed (no forward state is kept). bf16 layers round
+ * dY, dG/dU and H to bf16 as GEMM operands; every accumulation is fp32. A
+ * shared expert must have the routed width (MOE_ERR_UNSUPPORTED otherwise).
+ * T must be positive. Deterministic: no atomics; fixed reduction orders.
+ */
+moe_status moe_backward(const moe_layer *layer, const void *x, int64_t T, const int32_t *topk_idx,
+                        const float *topk_w, const float *dy, float z_loss_coef, float aux_loss_coef,
+                        const moe_grads *grads, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Phase timing (measurement only)                                         */
 /* ---------------------------------------------------------------------- */
 

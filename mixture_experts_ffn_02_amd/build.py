@@ -32,7 +32,7 @@ COMMON = [
 PER_FILE = {
     "route.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 
 
 def _compile(src: str) -> str:

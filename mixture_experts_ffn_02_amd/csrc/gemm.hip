@@ -164,8 +164,9 @@ void k_gemm(GemmLaunch g) {
   const int64_t chunk = (total + kXcd - 1) / kXcd;
   const int64_t L0 = xcd * chunk;
   const int64_t L1 = L0 + chunk < total ? L0 + chunk : total;
-  const size_t kbytes = (size_t)g.K * sizeof(DT);
-  const int nk = g.K / C::KE;
+  const bool kg = g.koffs != nullptr;  // K-grouped (weight-gradient) mode
+  const size_t kbytes = (size_t)(kg ? g.ld : g.K) * sizeof(DT);
+  const int nk_all = g.K / C::KE;
   const int group_m = g.group_m > 0 ? g.group_m : 8;
   // Position of this lane in a 1 KB DMA run: row lane / CPR of the run, LDS
   // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ key(row).
@@ -189,9 +190,15 @@ void k_gemm(GemmLaunch g) {
       const int2 t = g.tiles[tile_m];
       skip = t.x < 0 || t.x >= g.n_groups || t.y < 0;
       grp = skip ? 0 : t.x;
-      row0 = (int64_t)g.offsets[grp] + (int64_t)t.y * BM;
-      const int64_t left = (int64_t)g.offsets[grp + 1] - row0;
-      rows = (int)(left < BM ? left : BM);
+      if (kg) {
+        row0 = (int64_t)t.y * BM;
+        const int64_t left = (int64_t)g.m_valid - row0;
+        rows = (int)(left < BM ? left : BM);
+      } else {
+        row0 = (int64_t)g.offsets[grp] + (int64_t)t.y * BM;
+        const int64_t left = (int64_t)g.offsets[grp + 1] - row0;
+        rows = (int)(left < BM ? left : BM);
+      }
     } else {
       row0 = tile_m * BM;
       const int64_t left = g.rows - row0;
@@ -201,8 +208,12 @@ void k_gemm(GemmLaunch g) {
     const int n0 = tile_n * BN;
     const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
     const bool xg = grp == g.extra_group;
-    const unsigned char* B0 = xg ? reinterpret_cast<const unsigned char*>(g.bx0)
-                                 : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
+    // K range of this tile: the whole K, or the group's columns (K-grouped)
+    const int nk = kg ? (g.koffs[grp + 1] - g.koffs[grp]) / C::KE : nk_all;
+    const size_t kofs = kg ? (size_t)g.koffs[grp] * sizeof(DT) : 0;
+    const unsigned char* B0 = kg ? reinterpret_cast<const unsigned char*>(g.b0)
+                              : xg ? reinterpret_cast<const unsigned char*>(g.bx0)
+                                   : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
     const unsigned char* B1 = !GATEUP ? B0
                               : xg    ? reinterpret_cast<const unsigned char*>(g.bx1)
                                       : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes;
@@ -227,7 +238,7 @@ void k_gemm(GemmLaunch g) {
     const uint32_t lane_off = (uint32_t)((wave * C::RPR + lrow) * kbytes) + lchunk * 16;
     auto issue = [&](int kt) {
       unsigned char* sb = lds + (kt % NBUF) * C::STAGE + wave * C::RPR * SB;
-      const size_t off = (size_t)kt * SB;
+      const size_t off = kofs + (size_t)kt * SB;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
         lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + off + lchunk * 16, sb + i * 4 * C::RPR * SB);
@@ -345,47 +356,82 @@ void k_gemm(GemmLaunch g) {
 
     // Epilogue, one 32 x 32 accumulator tile at a time. Element e of a tile
     // sits in row 8*(e/4) + 4*(l/32) + e%4 and column l % 32 of lane l; the
-    // wave writes the tile (SwiGLU applied, converted to the output type) to
-    // its own LDS scratch, row-major with padded rows, and reads it back as
-    // 16-byte row chunks, so that each store covers contiguous columns.
+    // wave writes the tile (converted to the output type) to its own LDS
+    // scratch, row-major with padded rows, and reads it back as 16-byte row
+    // chunks, so that each store covers contiguous columns. `row_ptr(m)` is
+    // the output row of tile row m; rows at or past `rows` are not stored.
     {
+      static_assert(4 * 32 * (32 * 4 + 16) <= NBUF * C::STAGE, "epilogue scratch");
+      unsigned char* scr = lds + wave * 32 * (32 * 4 + 16);
+      auto put_tile = [&](auto zero, const f32x16& v, int i, int j, auto row_ptr) {
+        using T = decltype(zero);
+        constexpr int EB = (int)sizeof(T), P = 32 * EB + 16, CH = 32 * EB / 16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          T o;
+          if constexpr (sizeof(T) == 2)
+            o = f32_to_bf16(v[e]);
+          else
+            o = v[e];
+          *reinterpret_cast<T*>(scr + r * P + (lane & 31) * EB) = o;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int q0 = 0; q0 < 32 * CH; q0 += 64) {
+          const int q = q0 + lane, r = q / CH, c16 = q % CH;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(scr + r * P + c16 * 16);
+          const int m = wm * C::TM + i * 32 + r;
+          const int n = n0 + wn * C::TN + j * 32 + c16 * (16 / EB);
+          if (m < rows) *reinterpret_cast<u32x4*>(row_ptr(m) + (size_t)n * EB) = val;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
       using OT = typename Out<DT, GATEUP>::T;
-      constexpr int OB = (int)sizeof(OT);
-      constexpr int PITCH = 32 * OB + 16;
-      constexpr int CH = 32 * OB / 16;  // 16-byte chunks per row
-      static_assert(4 * 32 * PITCH <= NBUF * C::STAGE, "epilogue scratch");
-      unsigned char* scr = lds + wave * 32 * PITCH;
-      unsigned char* out = reinterpret_cast<unsigned char*>(g.out);
+      auto plain_row = [&](void* base, int eb) {
+        return [=](int m) { return reinterpret_cast<unsigned char*>(base) + (size_t)(row0 + m) * g.N * eb; };
+      };
+      // K-grouped output rows: group grp, row row0 + m of its m_rows
+      auto kg_row = [&](int m) {
+        const int mm = (int)row0 + m;
+        const bool second = g.m0 > 0 && mm >= g.m0;
+        const int rows0 = g.m0 > 0 ? g.m0 : g.m_rows;
+        unsigned char* base;
+        if (xg)
+          base = reinterpret_cast<unsigned char*>(second ? g.xout1 : g.xout0);
+        else if (second)
+          base = reinterpret_cast<unsigned char*>(g.out1) + (size_t)grp * (g.m_rows - g.m0) * g.N * 4;
+        else
+          base = reinterpret_cast<unsigned char*>(g.out) + (size_t)grp * rows0 * g.N * 4;
+        return base + (size_t)(second ? mm - g.m0 : mm) * g.N * 4;
+      };
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
+          if constexpr (GATEUP) {
+            f32x16 hv;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            OT v;
-            if constexpr (GATEUP) {
+            for (int e = 0; e < 16; ++e) {
               const float gv = acc[0][i][j][e], uv = acc[1][i][j][e];
-              v = to_out<DT>(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
-            } else {
-              v = acc[0][i][j][e];
+              hv[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             }
-            *reinterpret_cast<OT*>(scr + r * PITCH + (lane & 31) * OB) = v;
+            put_tile(OT{}, hv, i, j, plain_row(g.out, (int)sizeof(OT)));
+            if (g.out_g) {
+              put_tile(float{}, acc[0][i][j], i, j, plain_row(g.out_g, 4));
+              put_tile(float{}, acc[1][i][j], i, j, plain_row(g.out_u, 4));
+            }
+          } else {
+            if (kg)
+              put_tile(float{}, acc[0][i][j], i, j, kg_row);
+            else
+              put_tile(float{}, acc[0][i][j], i, j, plain_row(g.out, 4));
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-          for (int q0 = 0; q0 < 32 * CH; q0 += 64) {
-            const int q = q0 + lane, r = q / CH, c16 = q % CH;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(scr + r * PITCH + c16 * 16);
-            const int m = wm * C::TM + i * 32 + r;
-            const int n = n0 + wn * C::TN + j * 32 + c16 * (16 / OB);
-            if (m < rows) *reinterpret_cast<u32x4*>(out + ((size_t)(row0 + m) * g.N + n) * OB) = v;
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -409,7 +455,7 @@ int cu_count() {
 template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
-  if (g.N % BN || g.K % C::KE) return hipErrorInvalidValue;
+  if (g.N % BN || (!g.koffs && g.K % C::KE)) return hipErrorInvalidValue;
   int64_t blocks = (int64_t)cu_count() * C::OCC;
   blocks = (blocks + kXcd - 1) / kXcd * kXcd;
   if (!g.offsets) {
@@ -439,9 +485,24 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n) {
   return (avg >= 768 && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
 }
 
+int gemm_kg_bm(int m_rows) { return m_rows % 128 == 0 ? 128 : 64; }
+
 // gate/up: BN columns of H (gate and up rows staged together); down: BN output
-// columns. The widest tile that divides N.
+// columns. The widest tile that divides N. K-grouped launches (weight
+// gradients) take 128- or 64-row tiles by m_rows (gemm_kg_bm).
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
+  if (g.koffs) {
+    if (g.gateup || g.m_rows % gemm_kg_bm(g.m_rows) || g.N % 64) return hipErrorInvalidValue;
+    const bool wide = g.N % 128 == 0;
+    if (g.dtype == 1) {
+      if (gemm_kg_bm(g.m_rows) == 128)
+        return wide ? launch_t<uint16_t, false, 128, 128, 128, 2>(g, s) : launch_t<uint16_t, false, 128, 64, 128, 2>(g, s);
+      return wide ? launch_t<uint16_t, false, 64, 128, 128, 2>(g, s) : launch_t<uint16_t, false, 64, 64, 128, 2>(g, s);
+    }
+    if (gemm_kg_bm(g.m_rows) == 128)
+      return wide ? launch_t<float, false, 128, 128, 128, 2>(g, s) : launch_t<float, false, 128, 64, 128, 2>(g, s);
+    return wide ? launch_t<float, false, 64, 128, 128, 2>(g, s) : launch_t<float, false, 64, 64, 128, 2>(g, s);
+  }
   if (g.dtype == 1) {
     if (g.gateup) {
       if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2>(g, s);

@@ -26,6 +26,8 @@ struct RouteLaunch {
 int route_tokens_per_block(int E);
 size_t route_lds_bytes(int E, int k);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+// The fp32 logits alone ([T, E] into a.logits), the same fma chains as the router.
+hipError_t launch_logits(const RouteLaunch& a, hipStream_t s);
 // out[6] = z-loss, aux loss, cv, entropy (bits), max/mean load, unused share,
 // from the partials of launch_route (nb blocks) and the expert counts.
 hipError_t launch_router_metrics(const double* mpart, int nb, const int32_t* counts, int64_t T, int E, int k,
@@ -77,11 +79,50 @@ struct GemmLaunch {
   int64_t max_m_tiles;     // grid bound on m-tiles
   int group_m;             // row tiles per raster group (0: default)
   int64_t rows;            // dense mode: number of rows
+  // gate/up only: also store the fp32 pre-activations g and u ([rows, N]),
+  // which the backward pass needs
+  float* out_g = nullptr;
+  float* out_u = nullptr;
+  // K-grouped mode (weight gradients): group e of the tile list reduces over
+  // columns koffs[e] .. koffs[e+1]-1 (multiples of the K stage) of A [m_rows,
+  // ld] and B [N, ld]; its output is [m_rows, N] (rows >= m_valid are not
+  // stored); rows below m0 go to out + e*m0*N, the others to out1 +
+  // e*(m_rows-m0)*N (m0 = 0: all to out); the extra group writes to xout0 /
+  // xout1 instead. No row gather, no weight stacking.
+  const int32_t* koffs = nullptr;
+  int64_t ld = 0;
+  int m_rows = 0, m_valid = 0, m0 = 0;
+  void* out1 = nullptr;
+  void* xout0 = nullptr;
+  void* xout1 = nullptr;
 };
 // Row tile (128 or 256) for `rows` rows in `groups` groups and n output
 // columns; the tile list of a grouped launch must be built with the same value.
 int gemm_bm(int dtype, int64_t rows, int64_t groups, int n);
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s);
+
+// --------------------------------------------------------------- backward
+hipError_t launch_combine_bwd(int dtype, int64_t T, int d, int k, const float* dy, const float* yperm,
+                              const int32_t* row_of, const float* w, float* dtw, void* dyp, bool shared,
+                              hipStream_t s);
+hipError_t launch_swiglu_bwd(int dtype, int64_t rows, int f, const float* dh, const float* g, const float* u,
+                             void* dgu, hipStream_t s);
+hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const int32_t* row_of, bool shared,
+                             const float* dxr, float* dx, hipStream_t s);
+// out[b][c][col0 + r] = in[b][r][c] (r < R), 0 for R <= r < Rpad; dtype 0 fp32, 1 bf16
+hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* out, int64_t batch, int64_t R,
+                            int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s);
+// grouped rows (through row_map when given) into per-group zero-padded K segments of [C, ldo]
+hipError_t launch_transpose_groups(int dtype, const void* in, const int32_t* row_map, const int32_t* offsets,
+                                   const int32_t* koffs, int G, int C, int64_t max_cols, int64_t ldo, void* out,
+                                   hipStream_t s);
+hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_t* koffs, int2* tiles,
+                           int32_t* n_tiles, hipStream_t s);
+hipError_t launch_router_bwd(int64_t T, int E, int ep, int k, const float* logits, const int32_t* idx,
+                             const float* dtw, const int32_t* counts, int score, int renorm, float z_coef,
+                             float aux_coef, float* dl, hipStream_t s);
+// Row tile of a K-grouped launch with m_rows output rows.
+int gemm_kg_bm(int m_rows);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const int32_t* row_of, const float* w,

@@ -268,9 +268,315 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- backward
+
+constexpr int kKPad = 64;  // K-segment granularity of the weight-gradient GEMMs (a K stage)
+
+struct BwdLayout {
+  size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row;
+  size_t h, g, u, yperm, dyp, dh, dgu, dxp, wdt, wgut;
+  size_t koffs, kg_tiles, kg_n, xt, dyt, ht, dgut;
+  size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn;
+  size_t total;
+  int64_t nb, rows, gemm_rows, max_tiles, kp, tp, kg_tiles_max;
+  int G, ep;
+};
+
+BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
+  BwdLayout o{};
+  const int64_t E = L->n_experts, k = L->top_k, d = L->d_model, f = L->d_ff;
+  const bool shared = L->d_ff_shared > 0;
+  const int eb = elem_bytes(L->dtype);
+  o.G = (int)E + (shared ? 1 : 0);
+  o.rows = T * k;
+  o.gemm_rows = o.rows + (shared ? T : 0);
+  const int64_t tpb = hist_tokens_per_block();
+  o.nb = (T + tpb - 1) / tpb;
+  o.max_tiles = (o.gemm_rows + 127) / 128 + o.G;
+  o.kp = (o.gemm_rows + (int64_t)kKPad * o.G + kKPad - 1) / kKPad * kKPad;  // bound on the padded K columns
+  o.tp = (T + kKPad - 1) / kKPad * kKPad;
+  o.ep = (int)((E + 127) / 128 * 128);
+  const int64_t mt = (2 * f > d ? 2 * f : d) / 64;  // m-tiles per group, at most
+  o.kg_tiles_max = o.G * mt;
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p = align_up(p + bytes);
+    return at;
+  };
+  const size_t R = (size_t)o.gemm_rows;
+  o.hist = take(4 * (size_t)(o.nb * E));
+  o.base = take(4 * (size_t)(o.nb * E));
+  o.rank = take(4 * (size_t)o.rows);
+  o.counts = take(4 * (size_t)E);
+  o.offsets = take(4 * (size_t)(E + 2));
+  o.n_tiles = take(4);
+  o.tiles = take(sizeof(int2) * (size_t)o.max_tiles);
+  o.row_of = take(4 * (size_t)o.rows);
+  o.tok_of_row = take(4 * R);
+  o.h = take((size_t)eb * R * f);
+  o.g = take(4 * R * f);
+  o.u = take(4 * R * f);
+  o.yperm = take(4 * R * d);
+  o.dyp = take((size_t)eb * R * d);
+  o.dh = take(4 * R * f);
+  o.dgu = take((size_t)eb * R * 2 * f);
+  o.dxp = take(4 * R * d);
+  o.wdt = take((size_t)eb * o.G * f * d);
+  o.wgut = take((size_t)eb * o.G * d * 2 * f);
+  o.koffs = take(4 * (size_t)(o.G + 1));
+  o.kg_tiles = take(sizeof(int2) * (size_t)o.kg_tiles_max);
+  o.kg_n = take(4);
+  o.xt = take((size_t)eb * d * o.kp);
+  o.dyt = take((size_t)eb * d * o.kp);
+  o.ht = take((size_t)eb * f * o.kp);
+  o.dgut = take((size_t)eb * 2 * f * o.kp);
+  o.logits = take(4 * (size_t)(T * E));
+  o.dtw = take(4 * (size_t)o.rows);
+  o.dl = take(4 * (size_t)T * o.ep);
+  o.dlt = take(4 * (size_t)o.ep * o.tp);
+  o.xtr = take(4 * (size_t)d * o.tp);
+  o.wrt = take(4 * (size_t)d * o.ep);
+  o.dxr = take(4 * (size_t)(T * d));
+  o.rkoffs = take(4 * 2);
+  o.rtiles = take(sizeof(int2) * (size_t)(o.ep / 64));
+  o.rn = take(4);
+  o.total = p;
+  return o;
+}
+
+moe_status check_backward(const moe_layer* L, int64_t T) {
+  moe_status st = check_layer(L, true);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->top_k)) != MOE_OK) return st;
+  // the shared expert runs as one more group of the grouped GEMMs
+  if (L->d_ff_shared > 0 && L->d_ff_shared != L->d_ff) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)(L->top_k + 1) > 0x3FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_backward_workspace_size(const moe_layer* L, int64_t T, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID;
+  moe_status st = check_backward(L, T);
+  if (st != MOE_OK) return st;
+  *bytes = make_bwd_layout(L, T).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int32_t* topk_idx, const float* topk_w,
+                        const float* dy, float z_loss_coef, float aux_loss_coef, const moe_grads* gr, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status st = check_backward(L, T);
+  if (st != MOE_OK) return st;
+  if (!gr || !gr->dx || !gr->dw_router || !gr->dw_gate || !gr->dw_up || !gr->dw_down) return MOE_ERR_INVALID;
+  const bool shared = L->d_ff_shared > 0;
+  if (shared != (gr->dws_gate && gr->dws_up && gr->dws_down)) return MOE_ERR_INVALID;
+  if (T > 0 && (!x || !topk_idx || !topk_w || !dy || !aligned16(x) || !aligned16(dy) || !aligned16(gr->dx)))
+    return MOE_ERR_INVALID;
+  const BwdLayout lo = make_bwd_layout(L, T);
+  if (T > 0 && (!ws || ws_bytes < lo.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_ERR_INVALID;  // the gradients of an empty batch are not defined here
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, f = L->d_ff, dt = L->dtype, G = lo.G;
+  const int eb = elem_bytes(dt);
+  int32_t* hist = at<int32_t>(ws, lo.hist);
+  int32_t* rank = at<int32_t>(ws, lo.rank);
+  int32_t* base = at<int32_t>(ws, lo.base);
+  int32_t* counts = at<int32_t>(ws, lo.counts);
+  int32_t* offsets = at<int32_t>(ws, lo.offsets);
+  int32_t* n_tiles = at<int32_t>(ws, lo.n_tiles);
+  int2* tiles = at<int2>(ws, lo.tiles);
+  int32_t* row_of = at<int32_t>(ws, lo.row_of);
+  int32_t* tok_of_row = at<int32_t>(ws, lo.tok_of_row);
+  float* dtw = gr->d_topk_w ? gr->d_topk_w : at<float>(ws, lo.dtw);
+
+  // 1. dispatch of the given routing (shared expert as group E)
+  const int tpb = hist_tokens_per_block();
+  const int bm = gemm_bm(dt, lo.gemm_rows, G, f);
+  MOE_TRY(launch_hist_rank(topk_idx, T, k, E, hist, rank, s));
+  MOE_TRY(launch_scan(hist, (int)lo.nb, E, counts, offsets, base, bm, n_tiles, tiles, s, shared ? T : 0));
+  MOE_TRY(launch_scatter(topk_idx, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s, shared));
+
+  // 2. forward recompute: H and the pre-activations G, U; expert outputs Y
+  GemmLaunch gu{};
+  gu.dtype = dt;
+  gu.gateup = true;
+  gu.a = x;
+  gu.a_rows = tok_of_row;
+  gu.a_row_count = T;
+  gu.n_groups = G;
+  gu.b0 = L->w_gate;
+  gu.b1 = L->w_up;
+  if (shared) {
+    gu.extra_group = E;
+    gu.bx0 = L->ws_gate;
+    gu.bx1 = L->ws_up;
+  }
+  gu.out = at<void>(ws, lo.h);
+  gu.out_g = at<float>(ws, lo.g);
+  gu.out_u = at<float>(ws, lo.u);
+  gu.N = f;
+  gu.K = d;
+  gu.offsets = offsets;
+  gu.tiles = tiles;
+  gu.n_tiles = n_tiles;
+  gu.max_m_tiles = lo.max_tiles;
+  MOE_TRY(launch_gemm(gu, bm, s));
+  GemmLaunch dn = gu;
+  dn.gateup = false;
+  dn.a = at<void>(ws, lo.h);
+  dn.a_rows = nullptr;
+  dn.b0 = L->w_down;
+  dn.b1 = nullptr;
+  dn.bx0 = L->ws_down;
+  dn.bx1 = nullptr;
+  dn.out = at<void>(ws, lo.yperm);
+  dn.out_g = dn.out_u = nullptr;
+  dn.N = d;
+  dn.K = f;
+  MOE_TRY(launch_gemm(dn, bm, s));
+
+  // 3. combine^T: combine-weight gradients and the expert output gradients
+  MOE_TRY(launch_combine_bwd(dt, T, d, k, dy, at<float>(ws, lo.yperm), row_of, topk_w, dtw, at<void>(ws, lo.dyp),
+                             shared, s));
+
+  // 4. weights transposed once per call (the GEMM wants K-contiguous rows)
+  unsigned char* wdt = at<unsigned char>(ws, lo.wdt);
+  unsigned char* wgut = at<unsigned char>(ws, lo.wgut);
+  MOE_TRY(launch_transpose(dt, dt, L->w_down, wdt, E, d, d, f, d, 0, s));                 // [E, d, f] -> [E, f, d]
+  MOE_TRY(launch_transpose(dt, dt, L->w_gate, wgut, E, f, f, d, 2 * f, 0, s));           // [E, f, d] -> [E, d, 0:f]
+  MOE_TRY(launch_transpose(dt, dt, L->w_up, wgut, E, f, f, d, 2 * f, f, s));             //           -> [E, d, f:2f]
+  if (shared) {
+    MOE_TRY(launch_transpose(dt, dt, L->ws_down, wdt + (size_t)E * f * d * eb, 1, d, d, f, d, 0, s));
+    MOE_TRY(launch_transpose(dt, dt, L->ws_gate, wgut + (size_t)E * d * 2 * f * eb, 1, f, f, d, 2 * f, 0, s));
+    MOE_TRY(launch_transpose(dt, dt, L->ws_up, wgut + (size_t)E * d * 2 * f * eb, 1, f, f, d, 2 * f, f, s));
+  }
+
+  // 5. down^T: dH = dY W_down (grouped), then SwiGLU^T
+  GemmLaunch g1 = dn;
+  g1.a = at<void>(ws, lo.dyp);
+  g1.b0 = wdt;
+  g1.extra_group = -1;
+  g1.bx0 = nullptr;
+  g1.out = at<void>(ws, lo.dh);
+  g1.N = f;
+  g1.K = d;
+  MOE_TRY(launch_gemm(g1, bm, s));
+  MOE_TRY(launch_swiglu_bwd(dt, lo.gemm_rows, f, at<float>(ws, lo.dh), at<float>(ws, lo.g), at<float>(ws, lo.u),
+                            at<void>(ws, lo.dgu), s));
+
+  // 6. gate/up^T: dXp = [dG | dU] [W_gate^T ; W_up^T]^T (grouped, K = 2 f)
+  GemmLaunch g2 = g1;
+  g2.a = at<void>(ws, lo.dgu);
+  g2.b0 = wgut;
+  g2.out = at<void>(ws, lo.dxp);
+  g2.N = d;
+  g2.K = 2 * f;
+  MOE_TRY(launch_gemm(g2, bm, s));
+
+  // 7. router: logits, logit gradients, dW_router = dl^T x, dx_router = dl W_router
+  RouteLaunch rl{x, dt, T, d, E, k, L->score, L->renorm, L->w_router, nullptr, nullptr, nullptr, nullptr, nullptr,
+                 at<float>(ws, lo.logits)};
+  MOE_TRY(launch_logits(rl, s));
+  float* dl = at<float>(ws, lo.dl);
+  MOE_TRY(launch_router_bwd(T, E, lo.ep, k, at<float>(ws, lo.logits), topk_idx, dtw, counts, L->score, L->renorm,
+                            z_loss_coef, aux_loss_coef, dl, s));
+  float* dlt = at<float>(ws, lo.dlt);
+  float* xtr = at<float>(ws, lo.xtr);
+  float* wrt = at<float>(ws, lo.wrt);
+  MOE_TRY(launch_transpose(0, 0, dl, dlt, 1, T, lo.tp, lo.ep, lo.tp, 0, s));     // [T, ep] -> [ep, tp]
+  MOE_TRY(launch_transpose(dt, 0, x, xtr, 1, T, lo.tp, d, lo.tp, 0, s));         // [T, d] -> [d, tp] fp32
+  MOE_TRY(launch_transpose(0, 0, L->w_router, wrt, 1, E, lo.ep, d, lo.ep, 0, s)); // [E, d] -> [d, ep]
+  int32_t* rkoffs = at<int32_t>(ws, lo.rkoffs);
+  const int rbm = gemm_kg_bm(lo.ep);
+  // one K segment: every token (padded to tp with zero columns)
+  MOE_TRY(launch_kg_setup(1, nullptr, (int)lo.tp, lo.ep / rbm, rkoffs, at<int2>(ws, lo.rtiles), at<int32_t>(ws, lo.rn),
+                          s));
+  GemmLaunch rw{};
+  rw.dtype = 0;
+  rw.gateup = false;
+  rw.a = dlt;
+  rw.b0 = xtr;
+  rw.out = gr->dw_router;
+  rw.N = d;
+  rw.n_groups = 1;
+  rw.offsets = rkoffs;  // unused in K-grouped mode except as the "grouped" marker
+  rw.tiles = at<int2>(ws, lo.rtiles);
+  rw.n_tiles = at<int32_t>(ws, lo.rn);
+  rw.max_m_tiles = lo.ep / rbm;
+  rw.koffs = rkoffs;
+  rw.ld = lo.tp;
+  rw.m_rows = lo.ep;
+  rw.m_valid = E;
+  MOE_TRY(launch_gemm(rw, rbm, s));
+  GemmLaunch rx{};
+  rx.dtype = 0;
+  rx.gateup = false;
+  rx.a = dl;
+  rx.b0 = wrt;
+  rx.out = at<void>(ws, lo.dxr);
+  rx.N = d;
+  rx.K = lo.ep;
+  rx.rows = T;
+  MOE_TRY(launch_gemm(rx, 128, s));
+
+  // 8. gather^T: dx
+  MOE_TRY(launch_gather_bwd(T, d, k, at<float>(ws, lo.dxp), row_of, shared, at<float>(ws, lo.dxr), gr->dx, s));
+
+  // 9. weight gradients: per-group K segments of transposed activations
+  int32_t* koffs = at<int32_t>(ws, lo.koffs);
+  const int mt_d = d / gemm_kg_bm(d), mt_gu = 2 * f / gemm_kg_bm(2 * f);
+  unsigned char* xt = at<unsigned char>(ws, lo.xt);
+  unsigned char* dyt = at<unsigned char>(ws, lo.dyt);
+  unsigned char* ht = at<unsigned char>(ws, lo.ht);
+  unsigned char* dgut = at<unsigned char>(ws, lo.dgut);
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_d, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s));
+  MOE_TRY(launch_transpose_groups(dt, x, tok_of_row, offsets, koffs, G, d, lo.kp, lo.kp, xt, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dyp), nullptr, offsets, koffs, G, d, lo.kp, lo.kp, dyt, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.h), nullptr, offsets, koffs, G, f, lo.kp, lo.kp, ht, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dgu), nullptr, offsets, koffs, G, 2 * f, lo.kp, lo.kp, dgut,
+                                  s));
+  GemmLaunch wd{};  // dW_down[e] [d, f] = dY_e^T H_e
+  wd.dtype = dt;
+  wd.gateup = false;
+  wd.a = dyt;
+  wd.b0 = ht;
+  wd.out = gr->dw_down;
+  wd.N = f;
+  wd.n_groups = G;
+  wd.extra_group = shared ? E : -1;
+  wd.xout0 = gr->dws_down;
+  wd.offsets = offsets;
+  wd.tiles = at<int2>(ws, lo.kg_tiles);
+  wd.n_tiles = at<int32_t>(ws, lo.kg_n);
+  wd.max_m_tiles = lo.kg_tiles_max;
+  wd.koffs = koffs;
+  wd.ld = lo.kp;
+  wd.m_rows = d;
+  wd.m_valid = d;
+  MOE_TRY(launch_gemm(wd, gemm_kg_bm(d), s));
+  // dW_gate[e], dW_up[e] [f, d] = [dG_e | dU_e]^T X_e: one launch of 2f rows
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_gu, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s));
+  GemmLaunch wg = wd;
+  wg.a = dgut;
+  wg.b0 = xt;
+  wg.out = gr->dw_gate;
+  wg.out1 = gr->dw_up;
+  wg.xout0 = gr->dws_gate;
+  wg.xout1 = gr->dws_up;
+  wg.N = d;
+  wg.m_rows = 2 * f;
+  wg.m_valid = 2 * f;
+  wg.m0 = f;
+  MOE_TRY(launch_gemm(wg, gemm_kg_bm(2 * f), s));
+  return MOE_OK;
+}
+
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

@@ -753,6 +753,13 @@ hipError_t launch_bias_update(const int32_t* counts, int E, float rate, float* b
   return hipGetLastError();
 }
 
+hipError_t launch_logits(const RouteLaunch& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.d % kLogKC || !a.logits) return hipErrorInvalidValue;
+  const dim3 g((unsigned)((a.T + kLogTT - 1) / kLogTT), (unsigned)((a.E + kLogTE - 1) / kLogTE));
+  return a.dtype == 1 ? launch_k(k_logits<uint16_t>, g, 0, s, a) : launch_k(k_logits<float>, g, 0, s, a);
+}
+
 int hist_tokens_per_block() { return kHistTT; }
 
 hipError_t launch_hist_rank(const int32_t* idx, int64_t T, int k, int E, int32_t* hist, int32_t* rank,

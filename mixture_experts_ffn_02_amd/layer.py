@@ -195,6 +195,34 @@ class MoELayer:
         bias_update(counts, b, rate)
         return b
 
+    def backward(self, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, z_loss_coef: float = 0.0,
+                 aux_loss_coef: float = 0.0) -> Dict[str, torch.Tensor]:
+        """moe_backward: fp32 gradients of x, the router, the expert weights
+        (and the shared expert's) and the combine weights, for the routing
+        (idx, w) of the forward pass and dy = dL/dy [T, d] fp32."""
+        T = self._check_x(x)
+        c = self.cfg
+        E, k, d, f, fs = c.n_experts, c.top_k, c.d_model, c.d_ff, c.d_ff_s
+        dev = x.device
+        for name, t, shape, dt in (("idx", idx, (T, k), torch.int32), ("w", w, (T, k), torch.float32),
+                                   ("dy", dy, (T, d), torch.float32)):
+            if t.shape != shape or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous {dt} {shape}")
+        z = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+        g = {"dx": z(T, d), "dw_router": z(E, d), "dw_gate": z(E, f, d), "dw_up": z(E, f, d), "dw_down": z(E, d, f),
+             "d_topk_w": z(T, k)}
+        if fs:
+            g.update(dws_gate=z(fs, d), dws_up=z(fs, d), dws_down=z(d, fs))
+        gc = N.MoeGradsC(*[None if g.get(n) is None else g[n].data_ptr() for n, _ in N.MoeGradsC._fields_])
+        n = ctypes.c_size_t()
+        N.check(self.lib.moe_backward_workspace_size(ctypes.byref(self.c), T, ctypes.byref(n)),
+                "moe_backward_workspace_size")
+        ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=dev)
+        N.check(self.lib.moe_backward(ctypes.byref(self.c), _p(x), T, _p(idx), _p(w), _p(dy), float(z_loss_coef),
+                                      float(aux_loss_coef), ctypes.byref(gc), _p(ws), ws.numel(), _stream()),
+                "moe_backward")
+        return g
+
     def permute(self, x: torch.Tensor, idx: torch.Tensor, with_rows: bool = True) -> Dict[str, torch.Tensor]:
         T = self._check_x(x)
         k, E, d = self.cfg.top_k, self.cfg.n_experts, self.cfg.d_model

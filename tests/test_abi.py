@@ -130,6 +130,17 @@ def test_other_entry_points_reject(lib):
         assert lib.moe_route_ex(ctypes.byref(c), p, 10, ctypes.byref(o), p, p, None, p, 1 << 40, None) == 1
     assert lib.moe_route_ex(ctypes.byref(c), p, 0, ctypes.byref(metrics), p, p, None, p, 1 << 40, None) == 1
     assert lib.moe_forward_ex(ctypes.byref(c), None, 10, None, p, None, None, None, p, 1 << 40, None, None) == 1
+    # backward: gradients, shared-expert consistency, workspace, width of the shared expert
+    grads = N.MoeGradsC(*([FAKE] * 5 + [None] * 4))
+    assert lib.moe_backward(ctypes.byref(c), p, 10, p, p, p, 0.0, 0.0, None, p, 1 << 40, None) == 1
+    assert lib.moe_backward(ctypes.byref(c), p, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), None, 0, None) == 3
+    assert lib.moe_backward(ctypes.byref(c), None, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), p, 1 << 40,
+                            None) == 1
+    sh = layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=128)
+    assert lib.moe_backward(ctypes.byref(sh), p, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), p, 1 << 40, None) == 1
+    wide = layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=192)
+    n = ctypes.c_size_t()
+    assert lib.moe_backward_workspace_size(ctypes.byref(wide), 10, ctypes.byref(n)) == 2
     # controller: expert count and pointers
     assert lib.moe_bias_update(0, p, 1e-3, p, None) == 1
     assert lib.moe_bias_update(8, None, 1e-3, p, None) == 1
