@@ -149,7 +149,9 @@ __device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned cha
 
 // GROUPED: rows come from the tile list over group offsets (routed experts);
 // otherwise one dense group of g.rows rows (the shared expert).
-template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF>
+// BWD: the backward-pass variants (gate/up storing the fp32 pre-activations,
+// K-grouped weight gradients); the forward kernels compile without them.
+template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF, bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DT, GATEUP, BM, BN, SB, NBUF>::OCC)))
 void k_gemm(GemmLaunch g) {
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
@@ -164,7 +166,7 @@ void k_gemm(GemmLaunch g) {
   const int64_t chunk = (total + kXcd - 1) / kXcd;
   const int64_t L0 = xcd * chunk;
   const int64_t L1 = L0 + chunk < total ? L0 + chunk : total;
-  const bool kg = g.koffs != nullptr;  // K-grouped (weight-gradient) mode
+  const bool kg = BWD && g.koffs != nullptr;  // K-grouped (weight-gradient) mode
   const size_t kbytes = (size_t)(kg ? g.ld : g.K) * sizeof(DT);
   const int nk_all = g.K / C::KE;
   const int group_m = g.group_m > 0 ? g.group_m : 8;
@@ -421,7 +423,7 @@ void k_gemm(GemmLaunch g) {
               hv[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             }
             put_tile(OT{}, hv, i, j, plain_row(g.out, (int)sizeof(OT)));
-            if (g.out_g) {
+            if (BWD && g.out_g) {
               put_tile(float{}, acc[0][i][j], i, j, plain_row(g.out_g, 4));
               put_tile(float{}, acc[1][i][j], i, j, plain_row(g.out_u, 4));
             }
@@ -452,7 +454,7 @@ int cu_count() {
   return n;
 }
 
-template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF>
+template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF, bool BWD = false>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
   if (g.N % BN || (!g.koffs && g.K % C::KE)) return hipErrorInvalidValue;
@@ -466,9 +468,9 @@ hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
     blocks = need < blocks ? need : blocks;
   }
   if (g.offsets)
-    hipLaunchKernelGGL((k_gemm<DT, GATEUP, true, BM, BN, SB, NBUF>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, true, BM, BN, SB, NBUF, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL((k_gemm<DT, GATEUP, false, BM, BN, SB, NBUF>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, false, BM, BN, SB, NBUF, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -493,15 +495,26 @@ int gemm_kg_bm(int m_rows) { return m_rows % 128 == 0 ? 128 : 64; }
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
   if (g.koffs) {
     if (g.gateup || g.m_rows % gemm_kg_bm(g.m_rows) || g.N % 64) return hipErrorInvalidValue;
-    const bool wide = g.N % 128 == 0;
+    const bool wide = g.N % 128 == 0, tall = gemm_kg_bm(g.m_rows) == 128;
     if (g.dtype == 1) {
-      if (gemm_kg_bm(g.m_rows) == 128)
-        return wide ? launch_t<uint16_t, false, 128, 128, 128, 2>(g, s) : launch_t<uint16_t, false, 128, 64, 128, 2>(g, s);
-      return wide ? launch_t<uint16_t, false, 64, 128, 128, 2>(g, s) : launch_t<uint16_t, false, 64, 64, 128, 2>(g, s);
+      if (tall)
+        return wide ? launch_t<uint16_t, false, 128, 128, 128, 2, true>(g, s)
+                    : launch_t<uint16_t, false, 128, 64, 128, 2, true>(g, s);
+      return wide ? launch_t<uint16_t, false, 64, 128, 128, 2, true>(g, s)
+                  : launch_t<uint16_t, false, 64, 64, 128, 2, true>(g, s);
     }
-    if (gemm_kg_bm(g.m_rows) == 128)
-      return wide ? launch_t<float, false, 128, 128, 128, 2>(g, s) : launch_t<float, false, 128, 64, 128, 2>(g, s);
-    return wide ? launch_t<float, false, 64, 128, 128, 2>(g, s) : launch_t<float, false, 64, 64, 128, 2>(g, s);
+    if (tall)
+      return wide ? launch_t<float, false, 128, 128, 128, 2, true>(g, s) : launch_t<float, false, 128, 64, 128, 2, true>(g, s);
+    return wide ? launch_t<float, false, 64, 128, 128, 2, true>(g, s) : launch_t<float, false, 64, 64, 128, 2, true>(g, s);
+  }
+  if (g.out_g) {  // gate/up that also stores the pre-activations (backward recompute)
+    if (!g.gateup) return hipErrorInvalidValue;
+    if (g.dtype == 1) {
+      if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2, true>(g, s);
+      if (bm == 256) return launch_t<uint16_t, true, 256, 64, 128, 2, true>(g, s);
+      return launch_t<uint16_t, true, 128, 64, 128, 2, true>(g, s);
+    }
+    return launch_t<float, true, 128, 64, 128, 2, true>(g, s);
   }
   if (g.dtype == 1) {
     if (g.gateup) {
