@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     return ap.parse_args()
 
 
@@ -91,6 +92,35 @@ def phase_bytes_and_flops(cfg):
                 work[a][key] += work[s][key]
             del work[s]
     return work
+
+
+def measure_backward(cfg, layer, x, steps: int, warmup: int):
+    """moe_backward for the forward's routing and a seeded dy: ms per call
+    (HIP events on the layer's stream) and its algorithmic expert-GEMM work:
+    dgrad and wgrad of gate/up and down, 12 rows*d*d_ff flops (the forward
+    recompute inside the call, 6 rows*d*d_ff more, is not counted)."""
+    import numpy as np
+    import torch
+
+    fw = layer.forward(x)
+    dy = torch.from_numpy(np.random.default_rng(1).standard_normal((cfg.T, cfg.d_model)).astype(np.float32)).cuda()
+    for _ in range(warmup):
+        layer.backward(x, fw["idx"], fw["w"], dy)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        layer.backward(x, fw["idx"], fw["w"], dy)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    rows = cfg.T * cfg.top_k + (cfg.T if cfg.d_ff_s else 0)
+    flops = 12.0 * rows * cfg.d_model * cfg.d_ff
+    peak = PEAK_TFLOPS[cfg.dtype]
+    return {"ms": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "expert_gemm_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
+            "note": "one moe_backward call (forward recompute included in the time, not in the flops)"}
 
 
 def cpu_baseline(cfg, inputs, target_s: float):
@@ -215,6 +245,11 @@ def main():
     out["expert_weights"] = {"experts_used": used, "bytes": wbytes,
                              "gbs_over_expert_gemms": round(wbytes / (gemm_ms * 1e-3) / 1e9, 1),
                              "frac_hbm": round(wbytes / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if not args.no_backward:
+        # weights, fp32 gradients and the backward workspace must fit comfortably
+        bw_bytes = layer.backward_workspace_bytes(cfg.T) + 4 * 3 * cfg.n_experts * cfg.d_model * cfg.d_ff
+        if bw_bytes < 120e9:
+            out["backward"] = measure_backward(cfg, layer, x, max(1, args.steps // 2), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_seconds)
     print(json.dumps(out), flush=True)

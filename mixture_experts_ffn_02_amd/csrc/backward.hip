@@ -113,10 +113,12 @@ __global__ __launch_bounds__(256) void k_gather_bwd(int64_t T, int d, int k, con
 // Batched transpose through 32 x 32 LDS tiles:
 //   out[b][c][col0 + r] = in[b][r][c] for r < R, c < C; 0 for R <= r < Rpad.
 // in rows have C elements (batch stride R*C); out rows have ldo elements
-// (batch stride C*ldo).
-template <typename TI, typename TO>
+// (batch stride C*ldo). BLOCKED: out is instead the panelled matrix with C
+// rows, panels of `panel` rows and K capacity Rpad.
+template <typename TI, typename TO, bool BLOCKED>
 __global__ __launch_bounds__(256) void k_transpose(const TI* __restrict__ in, TO* __restrict__ out, int64_t R,
-                                                   int64_t Rpad, int C, int64_t ldo, int64_t col0) {
+                                                   int64_t Rpad, int C, int64_t ldo, int64_t col0, int panel) {
+  constexpr int KB = 128 / (int)sizeof(TO);
   __shared__ float tile[32][33];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   const int64_t r0 = (int64_t)blockIdx.x * 32;
@@ -133,67 +135,176 @@ __global__ __launch_bounds__(256) void k_transpose(const TI* __restrict__ in, TO
   for (int q = ty; q < 32; q += 8) {
     const int c = c0 + q;
     const int64_t r = r0 + tx;
-    if (c < C && r < Rpad) ob[(int64_t)c * ldo + col0 + r] = from_f32<TO>(tile[tx][q]);
+    if (c >= C || r >= Rpad) continue;
+    if constexpr (BLOCKED)
+      out[panel_offset(c, r, panel, Rpad, KB)] = from_f32<TO>(tile[tx][q]);
+    else
+      ob[(int64_t)c * ldo + col0 + r] = from_f32<TO>(tile[tx][q]);
   }
 }
 
-// Rows of grouped activations into per-group K segments of a transposed
-// matrix: out[c][koffs[e] + i] = in[src(offsets[e] + i)][c] for i < count_e,
-// 0 for count_e <= i < koffs[e+1] - koffs[e]; src is row_map[] when given.
-// The grid covers columns 0 .. koffs[G] in blocks of 32.
+// Rows of grouped activations into per-group zero-padded K segments of a
+// panelled matrix with C rows (panels of `panel` rows, K capacity kcap):
+// column koffs[e] + i holds row offsets[e] + i (through row_map when given)
+// for i < count_e, zeros up to koffs[e+1]. A block owns one K stage of
+// columns (kb = 128 bytes / element size) x 64 features, which lie in one
+// panel: the group of each column is looked up once, rows are read as 64
+// contiguous features and written as one contiguous 64 x kb block.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose_groups(const T* __restrict__ in, const int32_t* __restrict__ row_map,
                                                           const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ koffs, int G, int C,
-                                                          int64_t ldo, T* __restrict__ out) {
-  __shared__ float tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t q0 = (int64_t)blockIdx.x * 32;
-  const int c0 = blockIdx.y * 32;
+                                                          const int32_t* __restrict__ koffs, int G, int C, int panel,
+                                                          int64_t kcap, T* __restrict__ out) {
+  constexpr int KB = 128 / (int)sizeof(T);
+  __shared__ int64_t src[KB];
+  __shared__ float tile[KB][65];
+  const int tid = threadIdx.x;
+  const int64_t q0 = (int64_t)blockIdx.x * KB;
+  const int c0 = blockIdx.y * 64;
   const int64_t qend = koffs[G];
   if (q0 >= qend) return;  // uniform across the block
-  for (int q = ty; q < 32; q += 8) {
-    const int64_t col = q0 + q;
-    float v = 0.0f;
+  if (tid < KB) {
+    const int64_t col = q0 + tid;
+    int64_t sr = -1;
     if (col < qend) {
-      int lo = 0, hi = G - 1;  // group with koffs[e] <= col < koffs[e+1]
+      int lo = 0, hi = G - 1;  // last group with koffs[e] <= col
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (koffs[mid] <= col) lo = mid; else hi = mid - 1;
       }
       const int64_t i = col - koffs[lo];
       if (i < offsets[lo + 1] - offsets[lo]) {
-        int64_t src = offsets[lo] + i;
-        if (row_map) src = row_map[src];
-        if (c0 + tx < C) v = to_f32<T>(in[src * C + c0 + tx]);
+        sr = offsets[lo] + i;
+        if (row_map) sr = row_map[sr];
       }
     }
-    tile[q][tx] = v;
+    src[tid] = sr;
   }
   __syncthreads();
-  for (int q = ty; q < 32; q += 8) {
-    const int64_t col = q0 + tx;
-    if (col < qend && c0 + q < C) out[(int64_t)(c0 + q) * ldo + col] = from_f32<T>(tile[tx][q]);
+  for (int i = tid; i < KB * 64; i += 256) {
+    const int q = i >> 6, c = i & 63;
+    const int64_t sr = src[q];
+    tile[q][c] = (sr >= 0 && c0 + c < C) ? to_f32<T>(in[sr * C + c0 + c]) : 0.0f;
+  }
+  __syncthreads();
+  T* ob = out + panel_offset(c0, q0, panel, kcap, KB);  // row c0 + c at ob + c * KB
+  for (int i = tid; i < 64 * KB; i += 256) {
+    const int c = i / KB, q = i % KB;
+    if (c0 + c < C) ob[c * KB + q] = from_f32<T>(tile[q][c]);
   }
 }
+
+// out[i] = sum over segments s, in order, of part[s * seg_stride + i]
+__global__ __launch_bounds__(256) void k_sum_segments(const float* __restrict__ part, int nseg, int64_t seg_stride,
+                                                      int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.0f;
+  for (int s = 0; s < nseg; ++s) acc += part[s * seg_stride + i];
+  out[i] = acc;
+}
+
+constexpr int kKgMaxG = 2048;       // groups of a K-grouped launch, at most
+constexpr int kKgMaxRaster = 4096;  // raster groups for the XCD balance (more: equal tile counts)
+constexpr int kKgTileCost = 4;      // per-tile prologue and epilogue, in K stages
 
 // K segments of the weight-gradient GEMMs, one block: koffs[e] = sum over
 // groups before e of their row counts rounded up to kp (with no offsets: one
 // segment of kp columns); the tile list holds every (group, m-tile), empty
 // groups included (their gradient is zero).
+// A tile's work is its group's K stages plus kKgTileCost, so groups of
+// unequal size (skewed routing, the shared expert's T rows) give unequal
+// tiles. With xb, the raster order (as the GEMM walks it: raster groups of
+// kGroupM row tiles x ntn column tiles, row tile fastest) is cut into kXcd
+// ranges of about equal work, at whole columns of a raster group.
 __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restrict__ offsets, int kp, int mt,
                                                    int32_t* __restrict__ koffs, int2* __restrict__ tiles,
-                                                   int32_t* __restrict__ n_tiles) {
-  if (threadIdx.x == 0) {
+                                                   int32_t* __restrict__ n_tiles, int ntn, int ke,
+                                                   int32_t* __restrict__ xb) {
+  __shared__ int32_t ko[kKgMaxG + 1];
+  __shared__ int64_t rc[kKgMaxRaster + 1];  // prefix work of the raster groups
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
     int run = 0;
     for (int e = 0; e < G; ++e) {
+      ko[e] = run;
       koffs[e] = run;
       run += offsets ? (offsets[e + 1] - offsets[e] + kp - 1) / kp * kp : kp;
     }
+    ko[G] = run;
     koffs[G] = run;
     n_tiles[0] = G * mt;
   }
-  for (int i = threadIdx.x; i < G * mt; i += 1024) tiles[i] = make_int2(i / mt, i % mt);
+  for (int i = tid; i < G * mt; i += 1024) tiles[i] = make_int2(i / mt, i % mt);
+  if (!xb) return;  // uniform
+  const int64_t m_tiles = (int64_t)G * mt, total = m_tiles * ntn;
+  const int64_t nrg = (m_tiles + kGroupM - 1) / kGroupM;
+  if (nrg > kKgMaxRaster) {  // uniform: equal tile counts
+    if (tid <= kXcd) xb[tid] = (int32_t)((total + kXcd - 1) / kXcd * tid < total ? (total + kXcd - 1) / kXcd * tid : total);
+    return;
+  }
+  __syncthreads();
+  // work of one column of raster group r (its row tiles), per thread
+  auto col_work = [&](int64_t r) {
+    int64_t w = 0;
+    const int64_t m1 = (r + 1) * kGroupM < m_tiles ? (r + 1) * kGroupM : m_tiles;
+    for (int64_t m = r * kGroupM; m < m1; ++m) {
+      const int e = (int)(m / mt);
+      w += (ko[e + 1] - ko[e]) / ke + kKgTileCost;
+    }
+    return w;
+  };
+  // prefix sums: each thread a contiguous run of raster groups, then the runs
+  const int per = (int)((nrg + 1023) / 1024);
+  int64_t acc = 0;
+  for (int j = 0; j < per; ++j) {
+    const int64_t r = (int64_t)tid * per + j;
+    if (r < nrg) acc += col_work(r) * ntn;
+  }
+  part[tid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t run = 0;
+    for (int t = 0; t < 1024; ++t) {
+      const int64_t v = part[t];
+      part[t] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  {
+    int64_t run = part[tid];
+    for (int j = 0; j < per; ++j) {
+      const int64_t r = (int64_t)tid * per + j;
+      if (r < nrg) {
+        rc[r] = run;
+        run += col_work(r) * ntn;
+      }
+    }
+    if (tid == 1023) rc[nrg] = run;
+  }
+  __syncthreads();
+  if (tid <= kXcd) {
+    const int64_t all = rc[nrg];
+    int64_t L;
+    if (tid == 0) L = 0;
+    else if (tid == kXcd || all == 0) L = tid == kXcd ? total : total * tid / kXcd;
+    else {
+      const int64_t target = all * tid / kXcd;
+      int64_t lo = 0, hi = nrg - 1;  // last raster group starting at or before target
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (rc[mid] <= target) lo = mid; else hi = mid - 1;
+      }
+      const int64_t cw = col_work(lo);
+      int64_t cols = cw > 0 ? (target - rc[lo] + cw / 2) / cw : 0;
+      cols = cols > ntn ? ntn : cols;
+      const int64_t gm = (lo + 1) * kGroupM < m_tiles ? kGroupM : m_tiles - lo * kGroupM;
+      L = lo * (int64_t)kGroupM * ntn + cols * gm;
+    }
+    xb[tid] = (int32_t)L;
+  }
 }
 
 // Router logit gradients, one thread per token, in fp32: from the
@@ -301,41 +412,62 @@ hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const in
 }
 
 hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* out, int64_t batch, int64_t R,
-                            int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s) {
+                            int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s, int panel) {
   if (batch <= 0 || Rpad <= 0 || C <= 0) return hipSuccess;
+  const bool blocked = panel > 0;
+  const int kb = dtype_out == 1 ? 64 : 32;
+  if (blocked && (batch != 1 || C % panel || Rpad % kb)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((Rpad + 31) / 32), (unsigned)((C + 31) / 32), (unsigned)batch);
+#define MOE_TRANSPOSE(TI, TO)                                                                                        \
+  do {                                                                                                               \
+    if (blocked)                                                                                                     \
+      hipLaunchKernelGGL((k_transpose<TI, TO, true>), grid, dim3(256), 0, s, (const TI*)in, (TO*)out, R, Rpad, C,    \
+                         ldo, col0, panel);                                                                                 \
+    else                                                                                                             \
+      hipLaunchKernelGGL((k_transpose<TI, TO, false>), grid, dim3(256), 0, s, (const TI*)in, (TO*)out, R, Rpad, C,   \
+                         ldo, col0, panel);                                                                                 \
+  } while (0)
   if (dtype_in == 1 && dtype_out == 1)
-    hipLaunchKernelGGL((k_transpose<uint16_t, uint16_t>), grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out,
-                       R, Rpad, C, ldo, col0);
+    MOE_TRANSPOSE(uint16_t, uint16_t);
   else if (dtype_in == 1)
-    hipLaunchKernelGGL((k_transpose<uint16_t, float>), grid, dim3(256), 0, s, (const uint16_t*)in, (float*)out, R,
-                       Rpad, C, ldo, col0);
+    MOE_TRANSPOSE(uint16_t, float);
   else if (dtype_out == 1)
-    hipLaunchKernelGGL((k_transpose<float, uint16_t>), grid, dim3(256), 0, s, (const float*)in, (uint16_t*)out, R,
-                       Rpad, C, ldo, col0);
+    MOE_TRANSPOSE(float, uint16_t);
   else
-    hipLaunchKernelGGL((k_transpose<float, float>), grid, dim3(256), 0, s, (const float*)in, (float*)out, R, Rpad, C,
-                       ldo, col0);
+    MOE_TRANSPOSE(float, float);
+#undef MOE_TRANSPOSE
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_groups(int dtype, const void* in, const int32_t* row_map, const int32_t* offsets,
-                                   const int32_t* koffs, int G, int C, int64_t max_cols, int64_t ldo, void* out,
+                                   const int32_t* koffs, int G, int C, int panel, int64_t max_cols, void* out,
                                    hipStream_t s) {
   if (max_cols <= 0 || C <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((max_cols + 31) / 32), (unsigned)((C + 31) / 32));
+  const int kb = dtype == 1 ? 64 : 32;
+  if (panel <= 0 || panel % 64 || C % panel || max_cols % kb) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((max_cols + kb - 1) / kb), (unsigned)((C + 63) / 64));
   if (dtype == 1)
     hipLaunchKernelGGL(k_transpose_groups<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, row_map, offsets,
-                       koffs, G, C, ldo, (uint16_t*)out);
+                       koffs, G, C, panel, max_cols, (uint16_t*)out);
   else
     hipLaunchKernelGGL(k_transpose_groups<float>, grid, dim3(256), 0, s, (const float*)in, row_map, offsets, koffs,
-                       G, C, ldo, (float*)out);
+                       G, C, panel, max_cols, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_segments(const float* part, int nseg, int64_t seg_stride, int64_t n, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sum_segments, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nseg, seg_stride, n,
+                     out);
   return hipGetLastError();
 }
 
 hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_t* koffs, int2* tiles,
-                           int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_kg_setup, dim3(1), dim3(1024), 0, s, G, offsets, kp, mt, koffs, tiles, n_tiles);
+                           int32_t* n_tiles, hipStream_t s, int ntn, int ke, int32_t* xcd_bounds) {
+  if (G < 1 || G > kKgMaxG || mt < 1) return hipErrorInvalidValue;
+  if (xcd_bounds && (ntn < 1 || ke < 1 || (int64_t)G * mt * ntn > 0x7FFFFFFF)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_kg_setup, dim3(1), dim3(1024), 0, s, G, offsets, kp, mt, koffs, tiles, n_tiles, ntn, ke,
+                     xcd_bounds);
   return hipGetLastError();
 }
 

@@ -42,8 +42,6 @@
 namespace moe {
 namespace {
 
-constexpr int kXcd = 8;
-
 // Tile configuration. SB: bytes of one row in one LDS stage (64 or 128);
 // NBUF: LDS stage buffers.
 template <typename DT, bool GATEUP, int BM_, int BN_, int SB_, int NBUF_>
@@ -149,8 +147,9 @@ __device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned cha
 
 // GROUPED: rows come from the tile list over group offsets (routed experts);
 // otherwise one dense group of g.rows rows (the shared expert).
-// BWD: the backward-pass variants (gate/up storing the fp32 pre-activations,
-// K-grouped weight gradients); the forward kernels compile without them.
+// BWD: the backward-pass variants: gate/up that also stores the fp32
+// pre-activations (GATEUP), the K-grouped weight gradients (otherwise); the
+// forward kernels compile without them.
 template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF, bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DT, GATEUP, BM, BN, SB, NBUF>::OCC)))
 void k_gemm(GemmLaunch g) {
@@ -163,13 +162,23 @@ void k_gemm(GemmLaunch g) {
   const int64_t total = m_tiles * n_tiles_n;
   const int per_xcd = gridDim.x / kXcd;
   const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+  constexpr bool kg = BWD && !GATEUP && GROUPED;  // K-grouped (weight-gradient) mode
+  // This XCD's range of the raster order: equal shares of the tiles, or in
+  // K-grouped mode the ranges of equal work that launch_kg_setup computed
   const int64_t chunk = (total + kXcd - 1) / kXcd;
-  const int64_t L0 = xcd * chunk;
-  const int64_t L1 = L0 + chunk < total ? L0 + chunk : total;
-  const bool kg = BWD && g.koffs != nullptr;  // K-grouped (weight-gradient) mode
-  const size_t kbytes = (size_t)(kg ? g.ld : g.K) * sizeof(DT);
+  int64_t L0 = xcd * chunk;
+  int64_t L1 = L0 + chunk < total ? L0 + chunk : total;
+  if (kg && g.xcd_bounds) {
+    L0 = g.xcd_bounds[xcd];
+    L1 = g.xcd_bounds[xcd + 1];
+  }
+  // Row stride of the operands: a row of K elements, or in K-grouped mode one
+  // SB-byte piece (those operands are panelled: K stage s of the BM rows of
+  // an A tile is one block of BM * SB bytes, the panel of the tile holds its
+  // stages one after another, K capacity g.K; B likewise with BN rows)
+  const size_t kbytes = kg ? (size_t)SB : (size_t)g.K * sizeof(DT);
   const int nk_all = g.K / C::KE;
-  const int group_m = g.group_m > 0 ? g.group_m : 8;
+  const int group_m = g.group_m > 0 ? g.group_m : kGroupM;
   // Position of this lane in a 1 KB DMA run: row lane / CPR of the run, LDS
   // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ key(row).
   const int lrow = lane / C::CPR;
@@ -208,12 +217,14 @@ void k_gemm(GemmLaunch g) {
     }
     if (skip || rows <= 0) continue;  // uniform across the block
     const int n0 = tile_n * BN;
-    const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
+    // K-grouped: the tile's panels of A and B
+    const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a) +
+                             (kg ? (size_t)row0 * g.K * sizeof(DT) : (size_t)0);
     const bool xg = grp == g.extra_group;
     // K range of this tile: the whole K, or the group's columns (K-grouped)
     const int nk = kg ? (g.koffs[grp + 1] - g.koffs[grp]) / C::KE : nk_all;
-    const size_t kofs = kg ? (size_t)g.koffs[grp] * sizeof(DT) : 0;
-    const unsigned char* B0 = kg ? reinterpret_cast<const unsigned char*>(g.b0)
+    const int64_t st0 = kg ? (int64_t)g.koffs[grp] / C::KE : 0;  // first K stage of the group
+    const unsigned char* B0 = kg ? reinterpret_cast<const unsigned char*>(g.b0) + (size_t)n0 * g.K * sizeof(DT)
                               : xg ? reinterpret_cast<const unsigned char*>(g.bx0)
                                    : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
     const unsigned char* B1 = !GATEUP ? B0
@@ -228,28 +239,29 @@ void k_gemm(GemmLaunch g) {
     for (int i = 0; i < C::A_LOADS; ++i) {
       int r = (i * 4 + wave) * C::RPR + lrow;
       r = r < rows ? r : rows - 1;
-      int64_t src_row = row0 + r;
+      int64_t src_row = kg ? r : row0 + r;
       if (g.a_rows) {
         src_row = g.a_rows[src_row];
         src_row = src_row < 0 ? 0 : (src_row >= g.a_row_count ? g.a_row_count - 1 : src_row);
       }
       a_row[i] = (int32_t)src_row;
     }
-    const unsigned char* bbase0 = B0 + (size_t)n0 * kbytes;
-    const unsigned char* bbase1 = B1 + (size_t)n0 * kbytes;
+    const unsigned char* bbase0 = kg ? B0 : B0 + (size_t)n0 * kbytes;
+    const unsigned char* bbase1 = kg ? B1 : B1 + (size_t)n0 * kbytes;
     const uint32_t lane_off = (uint32_t)((wave * C::RPR + lrow) * kbytes) + lchunk * 16;
     auto issue = [&](int kt) {
       unsigned char* sb = lds + (kt % NBUF) * C::STAGE + wave * C::RPR * SB;
-      const size_t off = kofs + (size_t)kt * SB;
+      const size_t off_a = kg ? (size_t)(st0 + kt) * BM * SB : (size_t)kt * SB;
+      const size_t off_b = kg ? (size_t)(st0 + kt) * BN * SB : (size_t)kt * SB;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
-        lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + off + lchunk * 16, sb + i * 4 * C::RPR * SB);
+        lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + off_a + lchunk * 16, sb + i * 4 * C::RPR * SB);
 #pragma unroll
       for (int i = C::A_LOADS; i < C::LPS; ++i) {
         const int rb0 = (i - C::A_LOADS) * 4 * C::RPR;
         const unsigned char* src = (GATEUP && rb0 >= BN) ? bbase1 + (size_t)(rb0 - BN) * kbytes
                                                          : bbase0 + (size_t)rb0 * kbytes;
-        lds_dma16(src + lane_off + off, sb + i * 4 * C::RPR * SB);
+        lds_dma16(src + lane_off + off_b, sb + i * 4 * C::RPR * SB);
       }
     };
 
@@ -487,15 +499,30 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n) {
   return (avg >= 768 && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
 }
 
-int gemm_kg_bm(int m_rows) { return m_rows % 128 == 0 ? 128 : 64; }
+// Row tile of a K-grouped (weight-gradient) GEMM: bf16 takes 256 x 256 tiles
+// when m_rows and n divide and there are several such tiles per CU (each
+// tile then runs a group's whole K), else the largest of 128 and 64 that
+// divides m_rows.
+int gemm_kg_bm(int dtype, int m_rows, int n, int groups) {
+  if (dtype == 1 && m_rows % 256 == 0 && n % 256 == 0 &&
+      (int64_t)groups * (m_rows / 256) * (n / 256) >= 4 * (int64_t)cu_count())
+    return 256;
+  return m_rows % 128 == 0 ? 128 : 64;
+}
+
+// Column tile of a K-grouped launch: 256 with 256-row tiles, else the wider
+// of 128 and 64 that divides n.
+int gemm_kg_bn(int bm, int n) { return bm == 256 ? 256 : (n % 128 == 0 ? 128 : 64); }
 
 // gate/up: BN columns of H (gate and up rows staged together); down: BN output
 // columns. The widest tile that divides N. K-grouped launches (weight
-// gradients) take 128- or 64-row tiles by m_rows (gemm_kg_bm).
+// gradients) take the row tile bm from gemm_kg_bm.
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
   if (g.koffs) {
-    if (g.gateup || g.m_rows % gemm_kg_bm(g.m_rows) || g.N % 64) return hipErrorInvalidValue;
-    const bool wide = g.N % 128 == 0, tall = gemm_kg_bm(g.m_rows) == 128;
+    if (g.gateup || g.N % 64 || (bm != 64 && bm != 128 && bm != 256) || g.m_rows % bm) return hipErrorInvalidValue;
+    if (bm == 256 && (g.dtype != 1 || g.N % 256)) return hipErrorInvalidValue;
+    const bool wide = gemm_kg_bn(bm, g.N) == 128, tall = bm == 128;
+    if (bm == 256) return launch_t<uint16_t, false, 256, 256, 128, 2, true>(g, s);
     if (g.dtype == 1) {
       if (tall)
         return wide ? launch_t<uint16_t, false, 128, 128, 128, 2, true>(g, s)

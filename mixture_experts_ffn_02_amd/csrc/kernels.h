@@ -58,6 +58,9 @@ hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ------------------------------------------------------------------- GEMM
+constexpr int kXcd = 8;     // XCDs (L2 domains); workgroup i runs on XCD i % kXcd
+constexpr int kGroupM = 8;  // default row tiles per raster group
+
 struct GemmLaunch {
   int dtype;               // 0 fp32, 1 bf16 (operands; accumulation fp32)
   bool gateup;             // true: out = silu(A B0^T) * (A B1^T) in dtype; false: out = A B0^T in fp32
@@ -84,13 +87,15 @@ struct GemmLaunch {
   float* out_g = nullptr;
   float* out_u = nullptr;
   // K-grouped mode (weight gradients): group e of the tile list reduces over
-  // columns koffs[e] .. koffs[e+1]-1 (multiples of the K stage) of A [m_rows,
-  // ld] and B [N, ld]; its output is [m_rows, N] (rows >= m_valid are not
-  // stored); rows below m0 go to out + e*m0*N, the others to out1 +
-  // e*(m_rows-m0)*N (m0 = 0: all to out); the extra group writes to xout0 /
-  // xout1 instead. No row gather, no weight stacking.
+  // K columns koffs[e] .. koffs[e+1]-1 (multiples of the K stage) of A (m_rows
+  // rows) and B (N rows), both panelled with K capacity K >= koffs[G] and
+  // panels of BM (A) and BN (B) rows (see panel_offset). Its output is
+  // [m_rows, N] (rows >= m_valid are not stored); rows below m0 go to out +
+  // e*m0*N, the others to out1 + e*(m_rows-m0)*N (m0 = 0: all to out); the
+  // extra group writes to xout0 / xout1 instead. No row gather, no weight
+  // stacking.
   const int32_t* koffs = nullptr;
-  int64_t ld = 0;
+  const int32_t* xcd_bounds = nullptr;  // [kXcd + 1] ranges of the raster order per XCD (launch_kg_setup)
   int m_rows = 0, m_valid = 0, m0 = 0;
   void* out1 = nullptr;
   void* xout0 = nullptr;
@@ -109,20 +114,40 @@ hipError_t launch_swiglu_bwd(int dtype, int64_t rows, int f, const float* dh, co
                              void* dgu, hipStream_t s);
 hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const int32_t* row_of, bool shared,
                              const float* dxr, float* dx, hipStream_t s);
-// out[b][c][col0 + r] = in[b][r][c] (r < R), 0 for R <= r < Rpad; dtype 0 fp32, 1 bf16
+// Panelled operand of a K-grouped GEMM: rows in panels of P rows (one GEMM
+// tile), each panel K-blocked with K capacity kcap, so that a tile walks one
+// contiguous stretch of memory. Element (r, col), in elements, with kb = 128
+// bytes / element size (one K stage):
+__host__ __device__ inline int64_t panel_offset(int64_t r, int64_t col, int P, int64_t kcap, int kb) {
+  return (r / P) * P * kcap + (col / kb) * P * kb + (r % P) * kb + col % kb;
+}
+// out[b][c][col0 + r] = in[b][r][c] (r < R), 0 for R <= r < Rpad; dtype 0 fp32, 1 bf16.
+// panel > 0: out (one batch) is instead the panelled matrix with C rows,
+// panels of `panel` rows and K capacity Rpad (ldo, col0 unused).
 hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* out, int64_t batch, int64_t R,
-                            int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s);
-// grouped rows (through row_map when given) into per-group zero-padded K segments of [C, ldo]
+                            int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s, int panel = 0);
+// Grouped rows (through row_map when given) into per-group zero-padded K
+// segments (columns koffs[e] ..) of a panelled matrix with C rows, panels of
+// `panel` rows (a multiple of 64 dividing C) and K capacity max_cols.
 hipError_t launch_transpose_groups(int dtype, const void* in, const int32_t* row_map, const int32_t* offsets,
-                                   const int32_t* koffs, int G, int C, int64_t max_cols, int64_t ldo, void* out,
+                                   const int32_t* koffs, int G, int C, int panel, int64_t max_cols, void* out,
                                    hipStream_t s);
+// out[e][c] = sum over segments s (in order) of part[s][e][c], e < rows_out
+hipError_t launch_sum_segments(const float* part, int nseg, int64_t seg_stride, int64_t n, float* out, hipStream_t s);
+// K segments and tile list of a K-grouped launch: koffs[e] = sum over groups
+// before e of their row counts rounded up to kp (no offsets: kp each); tiles
+// = every (group, m-tile), mt m-tiles a group. With xcd_bounds: the ranges of
+// the launch's raster order (ntn column tiles, kGroupM row tiles a raster
+// group) that give each XCD an equal share of K stages (ke elements each).
 hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_t* koffs, int2* tiles,
-                           int32_t* n_tiles, hipStream_t s);
+                           int32_t* n_tiles, hipStream_t s, int ntn = 0, int ke = 0, int32_t* xcd_bounds = nullptr);
 hipError_t launch_router_bwd(int64_t T, int E, int ep, int k, const float* logits, const int32_t* idx,
                              const float* dtw, const int32_t* counts, int score, int renorm, float z_coef,
                              float aux_coef, float* dl, hipStream_t s);
-// Row tile of a K-grouped launch with m_rows output rows.
-int gemm_kg_bm(int m_rows);
+// Row tile and column tile of a K-grouped launch with m_rows output rows and
+// n columns: the panel heights of its A and B operands.
+int gemm_kg_bm(int dtype, int m_rows, int n, int groups);
+int gemm_kg_bn(int bm, int n);
 
 // ---------------------------------------------------------------- combine
 hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const int32_t* row_of, const float* w,

@@ -276,10 +276,10 @@ struct BwdLayout {
   size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row;
   size_t h, g, u, yperm, dyp, dh, dgu, dxp, wdt, wgut;
   size_t koffs, kg_tiles, kg_n, xt, dyt, ht, dgut;
-  size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn;
+  size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn, rpart, xb;
   size_t total;
-  int64_t nb, rows, gemm_rows, max_tiles, kp, tp, kg_tiles_max;
-  int G, ep;
+  int64_t nb, rows, gemm_rows, max_tiles, kp, tp, kg_tiles_max, rseg;
+  int G, ep, nseg;
 };
 
 BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
@@ -294,8 +294,21 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
   o.nb = (T + tpb - 1) / tpb;
   o.max_tiles = (o.gemm_rows + 127) / 128 + o.G;
   o.kp = (o.gemm_rows + (int64_t)kKPad * o.G + kKPad - 1) / kKPad * kKPad;  // bound on the padded K columns
-  o.tp = (T + kKPad - 1) / kKPad * kKPad;
   o.ep = (int)((E + 127) / 128 * 128);
+  // The router weight gradient dl^T x has few output tiles: it is split into
+  // nseg K segments of rseg tokens (about 512 tiles in all), summed in order.
+  {
+    const int64_t tpad = (T + kKPad - 1) / kKPad * kKPad;
+    const int64_t tiles = (o.ep / gemm_kg_bm(0, o.ep, d, 1)) * (d % 128 == 0 ? d / 128 : d / 64);
+    const int64_t want = (512 + tiles - 1) / tiles;
+    int64_t seg = (tpad + want - 1) / want;
+    seg = (seg + kKPad - 1) / kKPad * kKPad;
+    seg = seg < 256 ? 256 : seg;
+    seg = seg > tpad ? tpad : seg;
+    o.rseg = seg;
+    o.nseg = (int)((tpad + seg - 1) / seg);
+    o.tp = o.nseg * seg;
+  }
   const int64_t mt = (2 * f > d ? 2 * f : d) / 64;  // m-tiles per group, at most
   o.kg_tiles_max = o.G * mt;
   size_t p = 0;
@@ -338,9 +351,11 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
   o.xtr = take(4 * (size_t)d * o.tp);
   o.wrt = take(4 * (size_t)d * o.ep);
   o.dxr = take(4 * (size_t)(T * d));
-  o.rkoffs = take(4 * 2);
-  o.rtiles = take(sizeof(int2) * (size_t)(o.ep / 64));
+  o.rkoffs = take(4 * (size_t)(o.nseg + 1));
+  o.rtiles = take(sizeof(int2) * (size_t)o.nseg * (o.ep / 64));
   o.rn = take(4);
+  o.rpart = o.nseg > 1 ? take(4 * (size_t)o.nseg * o.ep * d) : 0;
+  o.xb = take(4 * (kXcd + 1));
   o.total = p;
   return o;
 }
@@ -489,31 +504,36 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   float* dlt = at<float>(ws, lo.dlt);
   float* xtr = at<float>(ws, lo.xtr);
   float* wrt = at<float>(ws, lo.wrt);
-  MOE_TRY(launch_transpose(0, 0, dl, dlt, 1, T, lo.tp, lo.ep, lo.tp, 0, s));     // [T, ep] -> [ep, tp]
-  MOE_TRY(launch_transpose(dt, 0, x, xtr, 1, T, lo.tp, d, lo.tp, 0, s));         // [T, d] -> [d, tp] fp32
+  // panelled transposes (panels of one GEMM tile), zero columns from T to tp
+  const int rbm = gemm_kg_bm(0, lo.ep, d, 1), rbn = gemm_kg_bn(rbm, d);
+  MOE_TRY(launch_transpose(0, 0, dl, dlt, 1, T, lo.tp, lo.ep, 0, 0, s, rbm));    // [T, ep] -> [ep, tp]
+  MOE_TRY(launch_transpose(dt, 0, x, xtr, 1, T, lo.tp, d, 0, 0, s, rbn));        // [T, d] -> [d, tp] fp32
   MOE_TRY(launch_transpose(0, 0, L->w_router, wrt, 1, E, lo.ep, d, lo.ep, 0, s)); // [E, d] -> [d, ep]
   int32_t* rkoffs = at<int32_t>(ws, lo.rkoffs);
-  const int rbm = gemm_kg_bm(lo.ep);
-  // one K segment: every token (padded to tp with zero columns)
-  MOE_TRY(launch_kg_setup(1, nullptr, (int)lo.tp, lo.ep / rbm, rkoffs, at<int2>(ws, lo.rtiles), at<int32_t>(ws, lo.rn),
-                          s));
+  // nseg K segments of rseg tokens each
+  MOE_TRY(launch_kg_setup(lo.nseg, nullptr, (int)lo.rseg, lo.ep / rbm, rkoffs, at<int2>(ws, lo.rtiles),
+                          at<int32_t>(ws, lo.rn), s, d / rbn, 32, at<int32_t>(ws, lo.xb)));
   GemmLaunch rw{};
   rw.dtype = 0;
   rw.gateup = false;
   rw.a = dlt;
   rw.b0 = xtr;
-  rw.out = gr->dw_router;
+  rw.out = lo.nseg > 1 ? at<void>(ws, lo.rpart) : gr->dw_router;
   rw.N = d;
-  rw.n_groups = 1;
+  rw.K = (int)lo.tp;  // K capacity of the panels
+  rw.n_groups = lo.nseg;
   rw.offsets = rkoffs;  // unused in K-grouped mode except as the "grouped" marker
   rw.tiles = at<int2>(ws, lo.rtiles);
   rw.n_tiles = at<int32_t>(ws, lo.rn);
-  rw.max_m_tiles = lo.ep / rbm;
+  rw.max_m_tiles = (int64_t)lo.nseg * (lo.ep / rbm);
   rw.koffs = rkoffs;
-  rw.ld = lo.tp;
+  rw.xcd_bounds = at<int32_t>(ws, lo.xb);
   rw.m_rows = lo.ep;
   rw.m_valid = E;
   MOE_TRY(launch_gemm(rw, rbm, s));
+  if (lo.nseg > 1)
+    MOE_TRY(launch_sum_segments(at<float>(ws, lo.rpart), lo.nseg, (int64_t)lo.ep * d, (int64_t)E * d, gr->dw_router,
+                                s));
   GemmLaunch rx{};
   rx.dtype = 0;
   rx.gateup = false;
@@ -530,16 +550,23 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
 
   // 9. weight gradients: per-group K segments of transposed activations
   int32_t* koffs = at<int32_t>(ws, lo.koffs);
-  const int mt_d = d / gemm_kg_bm(d), mt_gu = 2 * f / gemm_kg_bm(2 * f);
+  const int bm_d = gemm_kg_bm(dt, d, f, G), bm_gu = gemm_kg_bm(dt, 2 * f, d, G);
+  const int bn_d = gemm_kg_bn(bm_d, f), bn_gu = gemm_kg_bn(bm_gu, d);
+  const int mt_d = d / bm_d, mt_gu = 2 * f / bm_gu;
   unsigned char* xt = at<unsigned char>(ws, lo.xt);
   unsigned char* dyt = at<unsigned char>(ws, lo.dyt);
   unsigned char* ht = at<unsigned char>(ws, lo.ht);
   unsigned char* dgut = at<unsigned char>(ws, lo.dgut);
-  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_d, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s));
-  MOE_TRY(launch_transpose_groups(dt, x, tok_of_row, offsets, koffs, G, d, lo.kp, lo.kp, xt, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dyp), nullptr, offsets, koffs, G, d, lo.kp, lo.kp, dyt, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.h), nullptr, offsets, koffs, G, f, lo.kp, lo.kp, ht, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dgu), nullptr, offsets, koffs, G, 2 * f, lo.kp, lo.kp, dgut,
+  const int ke = dt == 1 ? 64 : 32;  // K elements of one stage
+  int32_t* xb = at<int32_t>(ws, lo.xb);
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_d, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s,
+                          f / bn_d, ke, xb));
+  // per-group zero-padded K segments, panelled for the GEMM that reads them
+  // (panels of its row or column tile, K capacity kp >= koffs[G])
+  MOE_TRY(launch_transpose_groups(dt, x, tok_of_row, offsets, koffs, G, d, bn_gu, lo.kp, xt, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dyp), nullptr, offsets, koffs, G, d, bm_d, lo.kp, dyt, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.h), nullptr, offsets, koffs, G, f, bn_d, lo.kp, ht, s));
+  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dgu), nullptr, offsets, koffs, G, 2 * f, bm_gu, lo.kp, dgut,
                                   s));
   GemmLaunch wd{};  // dW_down[e] [d, f] = dY_e^T H_e
   wd.dtype = dt;
@@ -548,6 +575,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wd.b0 = ht;
   wd.out = gr->dw_down;
   wd.N = f;
+  wd.K = (int)lo.kp;  // K capacity of the panels
   wd.n_groups = G;
   wd.extra_group = shared ? E : -1;
   wd.xout0 = gr->dws_down;
@@ -556,12 +584,13 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wd.n_tiles = at<int32_t>(ws, lo.kg_n);
   wd.max_m_tiles = lo.kg_tiles_max;
   wd.koffs = koffs;
-  wd.ld = lo.kp;
+  wd.xcd_bounds = xb;
   wd.m_rows = d;
   wd.m_valid = d;
-  MOE_TRY(launch_gemm(wd, gemm_kg_bm(d), s));
+  MOE_TRY(launch_gemm(wd, bm_d, s));
   // dW_gate[e], dW_up[e] [f, d] = [dG_e | dU_e]^T X_e: one launch of 2f rows
-  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_gu, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s));
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_gu, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s,
+                          d / bn_gu, ke, xb));
   GemmLaunch wg = wd;
   wg.a = dgut;
   wg.b0 = xt;
@@ -573,7 +602,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wg.m_rows = 2 * f;
   wg.m_valid = 2 * f;
   wg.m0 = f;
-  MOE_TRY(launch_gemm(wg, gemm_kg_bm(2 * f), s));
+  MOE_TRY(launch_gemm(wg, bm_gu, s));
   return MOE_OK;
 }
 

@@ -95,6 +95,7 @@ class MoELayer:
             setattr(c, name, None if tt is None else tt.data_ptr())
         self.c = c
         self._ws: Optional[torch.Tensor] = None
+        self._bws: Optional[torch.Tensor] = None
         self.device = tensors["w_router"].device
 
     @classmethod
@@ -195,6 +196,12 @@ class MoELayer:
         bias_update(counts, b, rate)
         return b
 
+    def backward_workspace_bytes(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        N.check(self.lib.moe_backward_workspace_size(ctypes.byref(self.c), T, ctypes.byref(n)),
+                "moe_backward_workspace_size")
+        return n.value
+
     def backward(self, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, z_loss_coef: float = 0.0,
                  aux_loss_coef: float = 0.0) -> Dict[str, torch.Tensor]:
         """moe_backward: fp32 gradients of x, the router, the expert weights
@@ -214,10 +221,11 @@ class MoELayer:
         if fs:
             g.update(dws_gate=z(fs, d), dws_up=z(fs, d), dws_down=z(d, fs))
         gc = N.MoeGradsC(*[None if g.get(n) is None else g[n].data_ptr() for n, _ in N.MoeGradsC._fields_])
-        n = ctypes.c_size_t()
-        N.check(self.lib.moe_backward_workspace_size(ctypes.byref(self.c), T, ctypes.byref(n)),
-                "moe_backward_workspace_size")
-        ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=dev)
+        need = max(1, self.backward_workspace_bytes(T))
+        if self._bws is None or self._bws.numel() < need:
+            self._bws = None
+            self._bws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = self._bws
         N.check(self.lib.moe_backward(ctypes.byref(self.c), _p(x), T, _p(idx), _p(w), _p(dy), float(z_loss_coef),
                                       float(aux_loss_coef), ctypes.byref(gc), _p(ws), ws.numel(), _stream()),
                 "moe_backward")

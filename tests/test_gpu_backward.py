@@ -57,6 +57,9 @@ CASES = [
       bias_range=0.5),
     C("bwd_bf16_softmax_e64", T=1000, d_model=128, n_experts=64, top_k=6, d_ff=128, bias_range=0.1),
     C("bwd_bf16_softmax_norenorm", T=257, d_model=64, n_experts=32, top_k=2, d_ff=64, renorm=False),
+    # enough 256 x 256 weight-gradient tiles (128 experts x 2 x 4 and x 8 x 2)
+    # for the wide K-grouped tile
+    C("bwd_bf16_wide_tiles", T=1024, d_model=512, n_experts=128, top_k=8, d_ff=1024, zipf_s=1.0),
 ]
 COEF = {"bwd_f32_softmax": (1e-3, 1e-3), "bwd_bf16_sigmoid_shared": (1e-3, 1e-3)}
 
