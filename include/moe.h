@@ -274,8 +274,9 @@ moe_status moe_backward_workspace_size(const moe_layer *layer, int64_t T, size_t
  * have no gradient.
  *   x        [T, d] layer dtype (the forward's input)
  *   topk_idx [T, k], topk_w [T, k]: the forward's outputs
- * Activations are recomputed (no forward state is kept). bf16 layers round
- * dY, dG/dU and H to bf16 as GEMM operands; every accumulation is fp32. A
+ * The gate/up activations are recomputed (no forward state is kept); the
+ * expert outputs are not needed (d_w = <h, dy W_down>). bf16 layers round dy,
+ * w dy, dG/dU and H to bf16 as GEMM operands; every accumulation is fp32. A
  * shared expert must have the routed width (MOE_ERR_UNSUPPORTED otherwise).
  * T must be positive. Deterministic: no atomics; fixed reduction orders.
  */

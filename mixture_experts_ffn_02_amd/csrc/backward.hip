@@ -5,9 +5,9 @@
 // "SigmoidRouter"; SpecForge PR #930, "What this adds") is
 //   y_t = sum_j w_tj E_{e_tj}(x_t) (+ S(x_t)),  E(x) = W_down (silu(W_gate x) * W_up x),
 // with w from the unbiased scores of the chosen experts. Given dy, the
-// backward runs
-//   combine^T : d_w[t,j] = <dy_t, Y[row]>, dY[row] = w[t,j] dy_t (shared row: dy_t)
-//   down^T    : dH = dY W_down           (grouped GEMM)
+// backward runs (row r = slot (t, j), or the shared row of t, weight 1)
+//   down^T    : dHu_r = dy_t W_down      (grouped GEMM gathering rows of dy)
+//   combine^T : d_w[t,j] = <h_r, dHu_r>  (which equals <dy_t, y_r>), dH_r = w dHu_r
 //   SwiGLU^T  : dG = dH u silu'(g), dU = dH silu(g)
 //   gate/up^T : dXp = dG W_gate + dU W_up (grouped GEMM, one K = 2 d_ff)
 //   gather^T  : dx_t = sum_j dXp[row_of[t,j]] (+ shared row) (+ router term)
@@ -41,56 +41,91 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
   return bf16_to_f32(v);
 }
 
-// One wave per token: for each slot, d_w = <dy_t, Y[row]> (lanes over
-// features, then a fixed xor-shuffle tree) and dY[row] = w dy_t in the
-// operand type; with a shared expert, dY[T*k + t] = dy_t.
-template <typename DT>
-__global__ __launch_bounds__(256) void k_combine_bwd(int64_t T, int d, int k, const float* __restrict__ dy,
-                                                     const float* __restrict__ yperm, const int32_t* __restrict__ row_of,
-                                                     const float* __restrict__ w, float* __restrict__ dtw,
-                                                     DT* __restrict__ dyp, int shared) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* dyt = dy + t * d;
-  for (int j = 0; j < k; ++j) {
-    const int64_t r = row_of[t * k + j];
-    const float wt = w[t * k + j];
-    float s = 0.0f;
-    for (int c = lane * 4; c < d; c += 256) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(dyt + c);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(yperm + r * d + c);
-      s = __builtin_fmaf(a[0], b[0], s);
-      s = __builtin_fmaf(a[1], b[1], s);
-      s = __builtin_fmaf(a[2], b[2], s);
-      s = __builtin_fmaf(a[3], b[3], s);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dyp[r * d + c + q] = from_f32<DT>(wt * a[q]);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0 && dtw) dtw[t * k + j] = s;
-  }
-  if (shared) {
-    const int64_t r = T * k + t;
-    for (int c = lane; c < d; c += 64) dyp[r * d + c] = from_f32<DT>(dyt[c]);
-  }
+// Four consecutive elements as fp32, and back.
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{bf16_to_f32((uint16_t)(v.x & 0xFFFF)), bf16_to_f32((uint16_t)(v.x >> 16)),
+               bf16_to_f32((uint16_t)(v.y & 0xFFFF)), bf16_to_f32((uint16_t)(v.y >> 16))};
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = o;
 }
 
-// dG = dH u s (1 + g (1 - s)), dU = dH g s with s = sigmoid(g), stored side
-// by side: dgu[r] = [dG_r | dU_r] (2 f values).
-template <typename DT>
-__global__ __launch_bounds__(256) void k_swiglu_bwd(int64_t rows, int f, const float* __restrict__ dh,
-                                                    const float* __restrict__ gp, const float* __restrict__ up,
-                                                    DT* __restrict__ dgu) {
+// dy in the operand type (bf16 layers): the down^T GEMM gathers its rows.
+__global__ __launch_bounds__(256) void k_to_bf16(int64_t n4, const float* __restrict__ in, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * f) return;
-  const int64_t r = i / f;
-  const int c = (int)(i % f);
-  const float g = gp[i], u = up[i], h = dh[i];
-  const float s = 1.0f / (1.0f + __expf(-g));
-  dgu[r * 2 * f + c] = from_f32<DT>(h * u * s * (1.0f + g * (1.0f - s)));
-  dgu[r * 2 * f + f + c] = from_f32<DT>(h * g * s);
+  if (i >= n4) return;
+  store4<uint16_t>(out + 4 * i, reinterpret_cast<const f32x4*>(in)[i]);
+}
+
+// One block per token t, its k routed rows (slot j: row row_of[t,j], weight
+// w[t,j]) and its shared-expert row (T*k + t, weight 1). The down^T GEMM gave
+// the unweighted dHu_r = dy_t W_down (the layer's expert output for the row
+// being y_r = h_r W_down^T). Per row:
+//   d_w[t,j] = <h_r, dHu_r>  (= <dy_t, y_r>; fixed-order block reduction)
+//   dH = w dHu;  dG = dH u s (1 + g (1 - s)),  dU = dH g s,  s = sigmoid(g)
+// stored side by side, dgu[r] = [dG_r | dU_r]; wrow[r] = w (the row's weight,
+// for the weight gradient of W_down).
+template <typename DT>
+__global__ __launch_bounds__(256) void k_swiglu_bwd(int64_t T, int k, int f, const float* __restrict__ dhu,
+                                                    const float* __restrict__ gp, const float* __restrict__ up,
+                                                    const DT* __restrict__ hp, const float* __restrict__ w,
+                                                    const int32_t* __restrict__ row_of, int shared,
+                                                    DT* __restrict__ dgu, float* __restrict__ dtw,
+                                                    float* __restrict__ wrow) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nj = k + (shared ? 1 : 0);
+  for (int j = 0; j < nj; ++j) {
+    const int64_t r = j < k ? (int64_t)row_of[t * k + j] : T * k + t;
+    const float wt = j < k ? w[t * k + j] : 1.0f;
+    float dot = 0.0f;
+    for (int c = tid * 4; c < f; c += 1024) {
+      const int64_t i = r * f + c;
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(dhu + i);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gp + i);
+      const f32x4 uv = *reinterpret_cast<const f32x4*>(up + i);
+      const f32x4 hv = load4<DT>(hp + i);
+      f32x4 dg, du;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dot = __builtin_fmaf(hv[q], dv[q], dot);
+        const float h = wt * dv[q], g = gv[q], u = uv[q];
+        const float s = 1.0f / (1.0f + __expf(-g));
+        dg[q] = h * u * s * (1.0f + g * (1.0f - s));
+        du[q] = h * g * s;
+      }
+      store4<DT>(dgu + r * 2 * f + c, dg);
+      store4<DT>(dgu + r * 2 * f + f + c, du);
+    }
+    if (j < k) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+      if (lane == 0) red[wave] = dot;
+      __syncthreads();
+      if (tid == 0 && dtw) dtw[t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
+      __syncthreads();
+    }
+    if (tid == 0) wrow[r] = wt;
+  }
 }
 
 // dx_t = sum_j dXp[row_of[t, j]] (slots in order) (+ dXp[T*k + t], the
@@ -110,36 +145,40 @@ __global__ __launch_bounds__(256) void k_gather_bwd(int64_t T, int d, int k, con
   *reinterpret_cast<f32x4*>(dx + t * d + c) = acc;
 }
 
-// Batched transpose through 32 x 32 LDS tiles:
+// Batched transpose through 64 x 64 LDS tiles (C and Rpad multiples of 64):
 //   out[b][c][col0 + r] = in[b][r][c] for r < R, c < C; 0 for R <= r < Rpad.
 // in rows have C elements (batch stride R*C); out rows have ldo elements
 // (batch stride C*ldo). BLOCKED: out is instead the panelled matrix with C
-// rows, panels of `panel` rows and K capacity Rpad.
+// rows, panels of `panel` rows and K capacity Rpad. 16-byte loads and stores.
 template <typename TI, typename TO, bool BLOCKED>
 __global__ __launch_bounds__(256) void k_transpose(const TI* __restrict__ in, TO* __restrict__ out, int64_t R,
                                                    int64_t Rpad, int C, int64_t ldo, int64_t col0, int panel) {
   constexpr int KB = 128 / (int)sizeof(TO);
-  __shared__ float tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  const int64_t r0 = (int64_t)blockIdx.x * 32;
-  const int c0 = blockIdx.y * 32;
+  constexpr int VI = 16 / (int)sizeof(TI), LI = 64 / VI, VO = 16 / (int)sizeof(TO), LO = 64 / VO;
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
   const int64_t b = blockIdx.z;
   const TI* ib = in + b * R * C;
   TO* ob = out + b * (int64_t)C * ldo;
-  for (int q = ty; q < 32; q += 8) {
+  for (int i = tid; i < 64 * LI; i += 256) {
+    const int q = i / LI, c = (i % LI) * VI;
     const int64_t r = r0 + q;
-    const int c = c0 + tx;
-    tile[q][tx] = (r < R && c < C) ? to_f32<TI>(ib[r * C + c]) : 0.0f;
+#pragma unroll
+    for (int v = 0; v < VI; v += 4) {
+      const f32x4 x = r < R ? load4<TI>(ib + r * C + c0 + c + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) tile[q][c + v + u] = x[u];
+    }
   }
   __syncthreads();
-  for (int q = ty; q < 32; q += 8) {
-    const int c = c0 + q;
-    const int64_t r = r0 + tx;
-    if (c >= C || r >= Rpad) continue;
-    if constexpr (BLOCKED)
-      out[panel_offset(c, r, panel, Rpad, KB)] = from_f32<TO>(tile[tx][q]);
-    else
-      ob[(int64_t)c * ldo + col0 + r] = from_f32<TO>(tile[tx][q]);
+  for (int i = tid; i < 64 * LO; i += 256) {
+    const int c = i / LO, q = (i % LO) * VO;  // out row c0 + c, columns r0 + q ..
+    TO* dst = BLOCKED ? out + panel_offset(c0 + c, r0 + q, panel, Rpad, KB) : ob + (int64_t)(c0 + c) * ldo + col0 + r0 + q;
+#pragma unroll
+    for (int v = 0; v < VO; v += 4)
+      store4<TO>(dst + v, f32x4{tile[q + v][c], tile[q + v + 1][c], tile[q + v + 2][c], tile[q + v + 3][c]});
   }
 }
 
@@ -150,13 +189,16 @@ __global__ __launch_bounds__(256) void k_transpose(const TI* __restrict__ in, TO
 // columns (kb = 128 bytes / element size) x 64 features, which lie in one
 // panel: the group of each column is looked up once, rows are read as 64
 // contiguous features and written as one contiguous 64 x kb block.
-template <typename T>
-__global__ __launch_bounds__(256) void k_transpose_groups(const T* __restrict__ in, const int32_t* __restrict__ row_map,
+// With scale, the value of grouped row i is multiplied by scale[i].
+template <typename TI, typename T>
+__global__ __launch_bounds__(256) void k_transpose_groups(const TI* __restrict__ in, const int32_t* __restrict__ row_map,
+                                                          const float* __restrict__ scale,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ koffs, int G, int C, int panel,
                                                           int64_t kcap, T* __restrict__ out) {
   constexpr int KB = 128 / (int)sizeof(T);
   __shared__ int64_t src[KB];
+  __shared__ float sc[KB];
   __shared__ float tile[KB][65];
   const int tid = threadIdx.x;
   const int64_t q0 = (int64_t)blockIdx.x * KB;
@@ -166,6 +208,7 @@ __global__ __launch_bounds__(256) void k_transpose_groups(const T* __restrict__ 
   if (tid < KB) {
     const int64_t col = q0 + tid;
     int64_t sr = -1;
+    float sv = 0.0f;
     if (col < qend) {
       int lo = 0, hi = G - 1;  // last group with koffs[e] <= col
       while (lo < hi) {
@@ -175,22 +218,41 @@ __global__ __launch_bounds__(256) void k_transpose_groups(const T* __restrict__ 
       const int64_t i = col - koffs[lo];
       if (i < offsets[lo + 1] - offsets[lo]) {
         sr = offsets[lo] + i;
+        sv = scale ? scale[sr] : 1.0f;
         if (row_map) sr = row_map[sr];
       }
     }
     src[tid] = sr;
+    sc[tid] = sv;
   }
   __syncthreads();
-  for (int i = tid; i < KB * 64; i += 256) {
-    const int q = i >> 6, c = i & 63;
+  // 16-byte loads: VI features each, 64 / VI per row
+  constexpr int VI = 16 / (int)sizeof(TI), LI = 64 / VI;
+  for (int i = tid; i < KB * LI; i += 256) {
+    const int q = i / LI, c = (i % LI) * VI;
     const int64_t sr = src[q];
-    tile[q][c] = (sr >= 0 && c0 + c < C) ? to_f32<T>(in[sr * C + c0 + c]) : 0.0f;
+    if (sr >= 0) {
+      const float a = sc[q];
+#pragma unroll
+      for (int v = 0; v < VI; v += 4) {
+        const f32x4 x = load4<TI>(in + sr * C + c0 + c + v);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tile[q][c + v + u] = a * x[u];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VI; ++v) tile[q][c + v] = 0.0f;
+    }
   }
   __syncthreads();
+  // 16-byte stores: VO columns each, KB / VO per row
+  constexpr int VO = 16 / (int)sizeof(T), LO = KB / VO;
   T* ob = out + panel_offset(c0, q0, panel, kcap, KB);  // row c0 + c at ob + c * KB
-  for (int i = tid; i < 64 * KB; i += 256) {
-    const int c = i / KB, q = i % KB;
-    if (c0 + c < C) ob[c * KB + q] = from_f32<T>(tile[q][c]);
+  for (int i = tid; i < 64 * LO; i += 256) {
+    const int c = i / LO, q = (i % LO) * VO;
+#pragma unroll
+    for (int v = 0; v < VO; v += 4)
+      store4<T>(ob + c * KB + q + v, f32x4{tile[q + v][c], tile[q + v + 1][c], tile[q + v + 2][c], tile[q + v + 3][c]});
   }
 }
 
@@ -202,6 +264,35 @@ __global__ __launch_bounds__(256) void k_sum_segments(const float* __restrict__ 
   float acc = 0.0f;
   for (int s = 0; s < nseg; ++s) acc += part[s * seg_stride + i];
   out[i] = acc;
+}
+
+// Exclusive prefix sum of x over the 1024 threads of a block (lane shuffles
+// inside each wave, then the 16 wave totals); *total gets the sum. tmp: 16
+// LDS slots.
+__device__ int64_t block_scan_1024(int64_t x, int64_t* tmp, int64_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t s = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(s, off);
+    if (lane >= off) s += y;
+  }
+  if (lane == 63) tmp[w] = s;
+  __syncthreads();
+  if (w == 0) {
+    int64_t t = lane < 16 ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int64_t y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < 16) tmp[lane] = t;
+  }
+  __syncthreads();
+  const int64_t before = w > 0 ? tmp[w - 1] : 0;
+  *total = tmp[15];
+  __syncthreads();  // tmp free for the next call
+  return before + s - x;
 }
 
 constexpr int kKgMaxG = 2048;       // groups of a K-grouped launch, at most
@@ -223,17 +314,23 @@ __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restr
                                                    int32_t* __restrict__ xb) {
   __shared__ int32_t ko[kKgMaxG + 1];
   __shared__ int64_t rc[kKgMaxRaster + 1];  // prefix work of the raster groups
-  __shared__ int64_t part[1024];
+  __shared__ int64_t tmp[16];
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < G; ++e) {
-      ko[e] = run;
-      koffs[e] = run;
-      run += offsets ? (offsets[e + 1] - offsets[e] + kp - 1) / kp * kp : kp;
+  int64_t carry = 0;
+  for (int e0 = 0; e0 < G; e0 += 1024) {  // uniform loop
+    const int e = e0 + tid;
+    const int64_t v = e < G ? (offsets ? (int64_t)(offsets[e + 1] - offsets[e] + kp - 1) / kp * kp : kp) : 0;
+    int64_t tot;
+    const int64_t ex = block_scan_1024(v, tmp, &tot);
+    if (e < G) {
+      ko[e] = (int32_t)(carry + ex);
+      koffs[e] = (int32_t)(carry + ex);
     }
-    ko[G] = run;
-    koffs[G] = run;
+    carry += tot;
+  }
+  if (tid == 0) {
+    ko[G] = (int32_t)carry;
+    koffs[G] = (int32_t)carry;
     n_tiles[0] = G * mt;
   }
   for (int i = tid; i < G * mt; i += 1024) tiles[i] = make_int2(i / mt, i % mt);
@@ -262,19 +359,9 @@ __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restr
     const int64_t r = (int64_t)tid * per + j;
     if (r < nrg) acc += col_work(r) * ntn;
   }
-  part[tid] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int t = 0; t < 1024; ++t) {
-      const int64_t v = part[t];
-      part[t] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
   {
-    int64_t run = part[tid];
+    int64_t tot;
+    int64_t run = block_scan_1024(acc, tmp, &tot);
     for (int j = 0; j < per; ++j) {
       const int64_t r = (int64_t)tid * per + j;
       if (r < nrg) {
@@ -378,28 +465,24 @@ __global__ __launch_bounds__(256) void k_router_bwd(int64_t T, int E, int ep, in
 
 }  // namespace
 
-hipError_t launch_combine_bwd(int dtype, int64_t T, int d, int k, const float* dy, const float* yperm,
-                              const int32_t* row_of, const float* w, float* dtw, void* dyp, bool shared,
-                              hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((T + 3) / 4));
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_combine_bwd<uint16_t>, grid, dim3(256), 0, s, T, d, k, dy, yperm, row_of, w, dtw,
-                       (uint16_t*)dyp, (int)shared);
-  else
-    hipLaunchKernelGGL(k_combine_bwd<float>, grid, dim3(256), 0, s, T, d, k, dy, yperm, row_of, w, dtw, (float*)dyp,
-                       (int)shared);
+hipError_t launch_to_bf16(int64_t n, const float* in, uint16_t* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, n / 4, in, out);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(int dtype, int64_t rows, int f, const float* dh, const float* g, const float* u,
-                             void* dgu, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows * f + 255) / 256));
+hipError_t launch_swiglu_bwd(int dtype, int64_t T, int k, int f, const float* dhu, const float* g, const float* u,
+                             const void* h, const float* w, const int32_t* row_of, bool shared, void* dgu, float* dtw,
+                             float* wrow, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (f % 4) return hipErrorInvalidValue;
   if (dtype == 1)
-    hipLaunchKernelGGL(k_swiglu_bwd<uint16_t>, grid, dim3(256), 0, s, rows, f, dh, g, u, (uint16_t*)dgu);
+    hipLaunchKernelGGL(k_swiglu_bwd<uint16_t>, dim3((unsigned)T), dim3(256), 0, s, T, k, f, dhu, g, u,
+                       (const uint16_t*)h, w, row_of, (int)shared, (uint16_t*)dgu, dtw, wrow);
   else
-    hipLaunchKernelGGL(k_swiglu_bwd<float>, grid, dim3(256), 0, s, rows, f, dh, g, u, (float*)dgu);
+    hipLaunchKernelGGL(k_swiglu_bwd<float>, dim3((unsigned)T), dim3(256), 0, s, T, k, f, dhu, g, u, (const float*)h,
+                       w, row_of, (int)shared, (float*)dgu, dtw, wrow);
   return hipGetLastError();
 }
 
@@ -417,7 +500,9 @@ hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* o
   const bool blocked = panel > 0;
   const int kb = dtype_out == 1 ? 64 : 32;
   if (blocked && (batch != 1 || C % panel || Rpad % kb)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((Rpad + 31) / 32), (unsigned)((C + 31) / 32), (unsigned)batch);
+  if (C % 64 || Rpad % 64 || Rpad < R || (!blocked && (ldo % 8 || col0 % 8 || col0 + Rpad > ldo)))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(Rpad / 64), (unsigned)(C / 64), (unsigned)batch);
 #define MOE_TRANSPOSE(TI, TO)                                                                                        \
   do {                                                                                                               \
     if (blocked)                                                                                                     \
@@ -439,19 +524,24 @@ hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* o
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_groups(int dtype, const void* in, const int32_t* row_map, const int32_t* offsets,
-                                   const int32_t* koffs, int G, int C, int panel, int64_t max_cols, void* out,
-                                   hipStream_t s) {
+hipError_t launch_transpose_groups(int dtype_in, int dtype, const void* in, const int32_t* row_map,
+                                   const float* scale, const int32_t* offsets, const int32_t* koffs, int G, int C,
+                                   int panel, int64_t max_cols, void* out, hipStream_t s) {
   if (max_cols <= 0 || C <= 0) return hipSuccess;
   const int kb = dtype == 1 ? 64 : 32;
-  if (panel <= 0 || panel % 64 || C % panel || max_cols % kb) return hipErrorInvalidValue;
+  if (panel <= 0 || panel % 64 || C % panel || max_cols % kb || C % 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((max_cols + kb - 1) / kb), (unsigned)((C + 63) / 64));
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_transpose_groups<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, row_map, offsets,
-                       koffs, G, C, panel, max_cols, (uint16_t*)out);
+  if (dtype == 1 && dtype_in == 1)
+    hipLaunchKernelGGL((k_transpose_groups<uint16_t, uint16_t>), grid, dim3(256), 0, s, (const uint16_t*)in, row_map,
+                       scale, offsets, koffs, G, C, panel, max_cols, (uint16_t*)out);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((k_transpose_groups<float, uint16_t>), grid, dim3(256), 0, s, (const float*)in, row_map,
+                       scale, offsets, koffs, G, C, panel, max_cols, (uint16_t*)out);
+  else if (dtype_in == 0)
+    hipLaunchKernelGGL((k_transpose_groups<float, float>), grid, dim3(256), 0, s, (const float*)in, row_map, scale,
+                       offsets, koffs, G, C, panel, max_cols, (float*)out);
   else
-    hipLaunchKernelGGL(k_transpose_groups<float>, grid, dim3(256), 0, s, (const float*)in, row_map, offsets, koffs,
-                       G, C, panel, max_cols, (float*)out);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

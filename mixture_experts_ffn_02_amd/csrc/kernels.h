@@ -107,11 +107,13 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n);
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s);
 
 // --------------------------------------------------------------- backward
-hipError_t launch_combine_bwd(int dtype, int64_t T, int d, int k, const float* dy, const float* yperm,
-                              const int32_t* row_of, const float* w, float* dtw, void* dyp, bool shared,
-                              hipStream_t s);
-hipError_t launch_swiglu_bwd(int dtype, int64_t rows, int f, const float* dh, const float* g, const float* u,
-                             void* dgu, hipStream_t s);
+hipError_t launch_to_bf16(int64_t n, const float* in, uint16_t* out, hipStream_t s);
+// Per token: d_w[t,j] = <h_r, dhu_r> for its routed rows r = row_of[t,j];
+// dgu[r] = [dG | dU] of dH = w dhu (w = 1 on the shared row T*k + t);
+// wrow[r] = w.
+hipError_t launch_swiglu_bwd(int dtype, int64_t T, int k, int f, const float* dhu, const float* g, const float* u,
+                             const void* h, const float* w, const int32_t* row_of, bool shared, void* dgu, float* dtw,
+                             float* wrow, hipStream_t s);
 hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const int32_t* row_of, bool shared,
                              const float* dxr, float* dx, hipStream_t s);
 // Panelled operand of a K-grouped GEMM: rows in panels of P rows (one GEMM
@@ -126,12 +128,13 @@ __host__ __device__ inline int64_t panel_offset(int64_t r, int64_t col, int P, i
 // panels of `panel` rows and K capacity Rpad (ldo, col0 unused).
 hipError_t launch_transpose(int dtype_in, int dtype_out, const void* in, void* out, int64_t batch, int64_t R,
                             int64_t Rpad, int C, int64_t ldo, int64_t col0, hipStream_t s, int panel = 0);
-// Grouped rows (through row_map when given) into per-group zero-padded K
-// segments (columns koffs[e] ..) of a panelled matrix with C rows, panels of
-// `panel` rows (a multiple of 64 dividing C) and K capacity max_cols.
-hipError_t launch_transpose_groups(int dtype, const void* in, const int32_t* row_map, const int32_t* offsets,
-                                   const int32_t* koffs, int G, int C, int panel, int64_t max_cols, void* out,
-                                   hipStream_t s);
+// Grouped rows (through row_map when given; times scale[row] when given)
+// into per-group zero-padded K segments (columns koffs[e] ..) of a panelled
+// matrix with C rows, panels of `panel` rows (a multiple of 64 dividing C)
+// and K capacity max_cols; in has dtype_in (fp32 into bf16 allowed).
+hipError_t launch_transpose_groups(int dtype_in, int dtype, const void* in, const int32_t* row_map,
+                                   const float* scale, const int32_t* offsets, const int32_t* koffs, int G, int C,
+                                   int panel, int64_t max_cols, void* out, hipStream_t s);
 // out[e][c] = sum over segments s (in order) of part[s][e][c], e < rows_out
 hipError_t launch_sum_segments(const float* part, int nseg, int64_t seg_stride, int64_t n, float* out, hipStream_t s);
 // K segments and tile list of a K-grouped launch: koffs[e] = sum over groups

@@ -274,7 +274,7 @@ constexpr int kKPad = 64;  // K-segment granularity of the weight-gradient GEMMs
 
 struct BwdLayout {
   size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row;
-  size_t h, g, u, yperm, dyp, dh, dgu, dxp, wdt, wgut;
+  size_t h, g, u, dyb, wrow, dh, dgu, dxp, wdt, wgut;
   size_t koffs, kg_tiles, kg_n, xt, dyt, ht, dgut;
   size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn, rpart, xb;
   size_t total;
@@ -330,8 +330,8 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
   o.h = take((size_t)eb * R * f);
   o.g = take(4 * R * f);
   o.u = take(4 * R * f);
-  o.yperm = take(4 * R * d);
-  o.dyp = take((size_t)eb * R * d);
+  o.dyb = L->dtype == 1 ? take(2 * (size_t)(T * d)) : 0;
+  o.wrow = take(4 * R);
   o.dh = take(4 * R * f);
   o.dgu = take((size_t)eb * R * 2 * f);
   o.dxp = take(4 * R * d);
@@ -417,7 +417,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   MOE_TRY(launch_scan(hist, (int)lo.nb, E, counts, offsets, base, bm, n_tiles, tiles, s, shared ? T : 0));
   MOE_TRY(launch_scatter(topk_idx, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s, shared));
 
-  // 2. forward recompute: H and the pre-activations G, U; expert outputs Y
+  // 2. forward recompute: H and the pre-activations G, U
   GemmLaunch gu{};
   gu.dtype = dt;
   gu.gateup = true;
@@ -442,23 +442,13 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
   MOE_TRY(launch_gemm(gu, bm, s));
-  GemmLaunch dn = gu;
-  dn.gateup = false;
-  dn.a = at<void>(ws, lo.h);
-  dn.a_rows = nullptr;
-  dn.b0 = L->w_down;
-  dn.b1 = nullptr;
-  dn.bx0 = L->ws_down;
-  dn.bx1 = nullptr;
-  dn.out = at<void>(ws, lo.yperm);
-  dn.out_g = dn.out_u = nullptr;
-  dn.N = d;
-  dn.K = f;
-  MOE_TRY(launch_gemm(dn, bm, s));
 
-  // 3. combine^T: combine-weight gradients and the expert output gradients
-  MOE_TRY(launch_combine_bwd(dt, T, d, k, dy, at<float>(ws, lo.yperm), row_of, topk_w, dtw, at<void>(ws, lo.dyp),
-                             shared, s));
+  // 3. dy in the operand type
+  const void* dya = dy;
+  if (dt == 1) {
+    MOE_TRY(launch_to_bf16((int64_t)T * d, dy, at<uint16_t>(ws, lo.dyb), s));
+    dya = at<void>(ws, lo.dyb);
+  }
 
   // 4. weights transposed once per call (the GEMM wants K-contiguous rows)
   unsigned char* wdt = at<unsigned char>(ws, lo.wdt);
@@ -472,22 +462,32 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
     MOE_TRY(launch_transpose(dt, dt, L->ws_up, wgut + (size_t)E * d * 2 * f * eb, 1, f, f, d, 2 * f, f, s));
   }
 
-  // 5. down^T: dH = dY W_down (grouped), then SwiGLU^T
-  GemmLaunch g1 = dn;
-  g1.a = at<void>(ws, lo.dyp);
+  // 5. down^T: dHu = dy W_down (grouped, rows gathered from dy, unweighted),
+  //    then combine^T and SwiGLU^T per token: d_w = <h, dHu>, dH = w dHu
+  GemmLaunch g1{};
+  g1.dtype = dt;
+  g1.gateup = false;
+  g1.a = dya;
+  g1.a_rows = tok_of_row;
+  g1.a_row_count = T;
+  g1.n_groups = G;
   g1.b0 = wdt;
-  g1.extra_group = -1;
-  g1.bx0 = nullptr;
   g1.out = at<void>(ws, lo.dh);
   g1.N = f;
   g1.K = d;
+  g1.offsets = offsets;
+  g1.tiles = tiles;
+  g1.n_tiles = n_tiles;
+  g1.max_m_tiles = lo.max_tiles;
   MOE_TRY(launch_gemm(g1, bm, s));
-  MOE_TRY(launch_swiglu_bwd(dt, lo.gemm_rows, f, at<float>(ws, lo.dh), at<float>(ws, lo.g), at<float>(ws, lo.u),
-                            at<void>(ws, lo.dgu), s));
+  float* wrow = at<float>(ws, lo.wrow);
+  MOE_TRY(launch_swiglu_bwd(dt, T, k, f, at<float>(ws, lo.dh), at<float>(ws, lo.g), at<float>(ws, lo.u),
+                            at<void>(ws, lo.h), topk_w, row_of, shared, at<void>(ws, lo.dgu), dtw, wrow, s));
 
   // 6. gate/up^T: dXp = [dG | dU] [W_gate^T ; W_up^T]^T (grouped, K = 2 f)
   GemmLaunch g2 = g1;
   g2.a = at<void>(ws, lo.dgu);
+  g2.a_rows = nullptr;
   g2.b0 = wgut;
   g2.out = at<void>(ws, lo.dxp);
   g2.N = d;
@@ -563,11 +563,13 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
                           f / bn_d, ke, xb));
   // per-group zero-padded K segments, panelled for the GEMM that reads them
   // (panels of its row or column tile, K capacity kp >= koffs[G])
-  MOE_TRY(launch_transpose_groups(dt, x, tok_of_row, offsets, koffs, G, d, bn_gu, lo.kp, xt, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dyp), nullptr, offsets, koffs, G, d, bm_d, lo.kp, dyt, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.h), nullptr, offsets, koffs, G, f, bn_d, lo.kp, ht, s));
-  MOE_TRY(launch_transpose_groups(dt, at<void>(ws, lo.dgu), nullptr, offsets, koffs, G, 2 * f, bm_gu, lo.kp, dgut,
+  // dY rows are w dy_t, formed here from the fp32 dy (one rounding)
+  MOE_TRY(launch_transpose_groups(dt, dt, x, tok_of_row, nullptr, offsets, koffs, G, d, bn_gu, lo.kp, xt, s));
+  MOE_TRY(launch_transpose_groups(0, dt, dy, tok_of_row, wrow, offsets, koffs, G, d, bm_d, lo.kp, dyt, s));
+  MOE_TRY(launch_transpose_groups(dt, dt, at<void>(ws, lo.h), nullptr, nullptr, offsets, koffs, G, f, bn_d, lo.kp, ht,
                                   s));
+  MOE_TRY(launch_transpose_groups(dt, dt, at<void>(ws, lo.dgu), nullptr, nullptr, offsets, koffs, G, 2 * f, bm_gu,
+                                  lo.kp, dgut, s));
   GemmLaunch wd{};  // dW_down[e] [d, f] = dY_e^T H_e
   wd.dtype = dt;
   wd.gateup = false;
