@@ -97,8 +97,8 @@ def phase_bytes_and_flops(cfg):
 def measure_backward(cfg, layer, x, steps: int, warmup: int):
     """moe_backward for the forward's routing and a seeded dy: ms per call
     (HIP events on the layer's stream) and its algorithmic expert-GEMM work:
-    dgrad and wgrad of gate/up and down, 12 rows*d*d_ff flops (the forward
-    recompute inside the call, 6 rows*d*d_ff more, is not counted)."""
+    dgrad and wgrad of gate/up and down, 12 rows*d*d_ff flops (the gate/up
+    recompute inside the call, 4 rows*d*d_ff more, is not counted)."""
     import numpy as np
     import torch
 
@@ -120,7 +120,7 @@ def measure_backward(cfg, layer, x, steps: int, warmup: int):
     return {"ms": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "expert_gemm_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
-            "note": "one moe_backward call (forward recompute included in the time, not in the flops)"}
+            "note": "one moe_backward call (gate/up recompute included in the time, not in the flops)"}
 
 
 def cpu_baseline(cfg, inputs, target_s: float):
@@ -200,8 +200,8 @@ def main():
     detail = {}
     for name, w in work.items():
         t_s = phase_ms[name] * 1e-3
-        if t_s <= 0:
-            continue
+        if t_s <= 0 or not (w.get("flops") or w.get("bytes")):
+            continue  # a phase that launched nothing (no shared expert)
         e = {"ms": round(phase_ms[name], 4)}
         if "flops" in w and w["flops"]:
             tf = w["flops"] / t_s / 1e12
@@ -213,6 +213,8 @@ def main():
         detail[name] = e
     for name in ("scan", "scatter"):
         detail[name] = {"ms": round(phase_ms[name], 4)}
+    # expert GEMM phases that ran (the shared expert's own launches only when it has them)
+    gemm_phases = [n for n in ("gateup", "down", "shared_gateup", "shared_down") if n in work and work[n]["flops"]]
 
     out = {
         "metric": METRIC,
@@ -233,15 +235,14 @@ def main():
         "roofline": roofline,
         "phases": detail,
         "grouped_gemm_frac_mfma": round(
-            sum(work[n]["flops"] for n in ("gateup", "down", "shared_gateup", "shared_down") if n in work)
-            / ((phase_ms["gateup"] + phase_ms["down"] + phase_ms["shared_gateup"] + phase_ms["shared_down"]) * 1e-3)
+            sum(work[n]["flops"] for n in gemm_phases) / (sum(phase_ms[n] for n in gemm_phases) * 1e-3)
             / 1e12 / peak, 4),
     }
     # expert weights the step had to read: experts that received tokens (+ the shared one)
     counts = layer.route(x)["counts"].cpu().numpy()
     used = int((counts > 0).sum())
     wbytes = (2 if cfg.dtype == "bf16" else 4) * 3 * cfg.d_model * (used * cfg.d_ff + cfg.d_ff_s)
-    gemm_ms = phase_ms["gateup"] + phase_ms["down"] + phase_ms["shared_gateup"] + phase_ms["shared_down"]
+    gemm_ms = sum(phase_ms[n] for n in gemm_phases)
     out["expert_weights"] = {"experts_used": used, "bytes": wbytes,
                              "gbs_over_expert_gemms": round(wbytes / (gemm_ms * 1e-3) / 1e9, 1),
                              "frac_hbm": round(wbytes / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
