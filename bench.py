@@ -1,13 +1,15 @@
 """Throughput of the MoE FFN layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload small_sigmoid]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload small_sigmoid]
 
 One step is one moe_forward call (route, dispatch, routed and shared SwiGLU
 experts, combine) over one batch of seeded synthetic tokens that are already
 resident in HBM. Prints one JSON line with the whole-job throughput, the
-per-phase times measured with hipEvents on the layer's stream inside the
-timed region, the roofline of the dominant kernel (the routed gate/up grouped
-GEMM), and the CPU oracle timed on a bounded sample of the same workload.
+roofline of the dominant kernel (the routed gate/up grouped GEMM, timed with
+hipEvents on the layer's stream around each of its launches in the timed
+region), per-phase times from a second pass of the same steps with every
+phase boundary timed, the backward pass, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -31,8 +33,8 @@ COPY_BYTES = 256 << 20  # plain device-to-device copy used to calibrate HBM coun
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="small_sigmoid")
     ap.add_argument("--tokens", type=int, default=0, help="override the workload's token count (small-T sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
@@ -168,7 +170,10 @@ def main():
     layer.workspace(cfg.T)
     for _ in range(args.warmup):
         layer.forward(x, y, want_routing=False)
-    timings = [Timing() for _ in range(args.steps)]
+    # Timed region: the gate/up launch of every step is bracketed by two
+    # hipEvents on the layer's stream (each event between kernels costs a
+    # few microseconds of stream time, so no other phase is timed here).
+    timings = [Timing(phases=["gateup"]) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -176,6 +181,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    gateup_ms = float(np.mean([t.read()["gateup"] for t in timings]))
+    for t in timings:
+        t.close()
+    # Phase breakdown: the same steps again with every boundary timed
+    timings = [Timing() for _ in range(min(args.steps, 10))]
+    for t in timings:
+        layer.forward(x, y, want_routing=False, timing=t)
+    torch.cuda.synchronize()
     if args.copy_calibration:
         # a plain elementwise copy (16 bytes per lane, whole grid) of known size
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -191,7 +204,7 @@ def main():
 
     work = phase_bytes_and_flops(cfg)
     peak = PEAK_TFLOPS[cfg.dtype]
-    gu = work["gateup"]["flops"] / (phase_ms["gateup"] * 1e-3) / 1e12
+    gu = work["gateup"]["flops"] / (gateup_ms * 1e-3) / 1e12
     traffic = traffic_from_profile("gateup", args.workload)
     what = "routed experts + the shared expert as one more group" if shared_as_group(cfg) else "routed experts"
     roofline = {"bound": "mfma", "kernel": f"k_gemm<{cfg.dtype}, gate/up, grouped> ({what})",
@@ -250,7 +263,7 @@ def main():
         # weights, fp32 gradients and the backward workspace must fit comfortably
         bw_bytes = layer.backward_workspace_bytes(cfg.T) + 4 * 3 * cfg.n_experts * cfg.d_model * cfg.d_ff
         if bw_bytes < 120e9:
-            out["backward"] = measure_backward(cfg, layer, x, max(1, args.steps // 2), 2)
+            out["backward"] = measure_backward(cfg, layer, x, max(1, min(args.steps // 4, 50)), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -305,8 +305,15 @@ moe_status moe_backward(const moe_layer *layer, const void *x, int64_t T, const 
 moe_status moe_timing_create(moe_timing **out);
 moe_status moe_timing_destroy(moe_timing *t);
 
+/* Time only the phases in phase_mask (bit p = phase p; default all). Each
+ * event recorded between two kernels costs a few microseconds of stream
+ * time, so a caller timing one phase records only that phase's two
+ * boundaries. MOE_ERR_INVALID for an empty mask or bits past the last phase. */
+moe_status moe_timing_select(moe_timing *t, uint32_t phase_mask);
+
 /* Milliseconds spent in each phase by the last moe_forward_ex call that
- * used `t`; waits for its events. phase_ms: host array of MOE_N_PHASES. */
+ * used `t`; waits for its events. phase_ms: host array of MOE_N_PHASES;
+ * phases outside the mask read -1. */
 moe_status moe_timing_read(moe_timing *t, float *phase_ms);
 
 #ifdef __cplusplus

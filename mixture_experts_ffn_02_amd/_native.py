@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_E
 EXPORTS = (
     "moe_status_str", "moe_workspace_size", "moe_route", "moe_route_ex", "moe_bias_update", "moe_permute",
     "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_forward_ex",
-    "moe_timing_create", "moe_timing_destroy", "moe_timing_read", "moe_backward_workspace_size", "moe_backward",
+    "moe_timing_create", "moe_timing_destroy", "moe_timing_read", "moe_timing_select", "moe_backward_workspace_size", "moe_backward",
 )
 
 
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.moe_timing_destroy.argtypes = [vp]
     L.moe_forward_ex.argtypes = [LP, vp, i64, OP, vp, vp, vp, vp, vp, sz, vp, vp]
     L.moe_timing_read.argtypes = [vp, P(ctypes.c_float)]
+    L.moe_timing_select.argtypes = [vp, ctypes.c_uint32]
     L.moe_backward_workspace_size.argtypes = [LP, i64, P(sz)]
     L.moe_backward.argtypes = [LP, vp, i64, vp, vp, vp, ctypes.c_float, ctypes.c_float, P(MoeGradsC), vp, sz, vp]
     for name in EXPORTS:

@@ -117,12 +117,13 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 struct moe_timing {
   hipEvent_t ev[MOE_N_PHASES + 1];
+  uint32_t mask;  // phases timed; boundary i is recorded when phase i or phase i-1 is
 };
 
 namespace {
 
 void mark(moe_timing* t, int i, hipStream_t s) {
-  if (t) (void)hipEventRecord(t->ev[i], s);
+  if (t && (((t->mask << 1) >> i) & 3u)) (void)hipEventRecord(t->ev[i], s);  // phase i or i-1 timed
 }
 
 moe_status check_T(int64_t T, int k) {
@@ -798,7 +799,14 @@ moe_status moe_timing_create(moe_timing** out) {
       return MOE_ERR_HIP;
     }
   }
+  t->mask = (1u << MOE_N_PHASES) - 1u;
   *out = t;
+  return MOE_OK;
+}
+
+moe_status moe_timing_select(moe_timing* t, uint32_t phase_mask) {
+  if (!t || phase_mask == 0 || (phase_mask >> MOE_N_PHASES)) return MOE_ERR_INVALID;
+  t->mask = phase_mask;
   return MOE_OK;
 }
 
@@ -811,10 +819,13 @@ moe_status moe_timing_destroy(moe_timing* t) {
 
 moe_status moe_timing_read(moe_timing* t, float* phase_ms) {
   if (!t || !phase_ms) return MOE_ERR_INVALID;
-  if (hipEventSynchronize(t->ev[MOE_N_PHASES]) != hipSuccess) return MOE_ERR_HIP;
+  int last = 0;  // the latest boundary recorded
+  for (int i = 0; i <= MOE_N_PHASES; ++i)
+    if (((t->mask << 1) >> i) & 3u) last = i;
+  if (hipEventSynchronize(t->ev[last]) != hipSuccess) return MOE_ERR_HIP;
   for (int i = 0; i < MOE_N_PHASES; ++i) {
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, t->ev[i], t->ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
+    float ms = -1.0f;
+    if (((t->mask >> i) & 1u) && hipEventElapsedTime(&ms, t->ev[i], t->ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
     phase_ms[i] = ms;
   }
   return MOE_OK;

@@ -6,7 +6,7 @@ is a call into the C ABI (include/moe.h), whose kernels do all the work.
 from __future__ import annotations
 
 import ctypes
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import numpy as np
 import torch
@@ -51,18 +51,25 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 class Timing:
-    """Per-phase hipEvent timing of moe_forward_ex."""
+    """Per-phase hipEvent timing of moe_forward_ex; `phases` (names from
+    N.PHASES) limits the events to those phases' boundaries."""
 
-    def __init__(self):
+    def __init__(self, phases: Optional[Sequence[str]] = None):
         self.lib = N.load()
         h = ctypes.c_void_p()
         N.check(self.lib.moe_timing_create(ctypes.byref(h)), "moe_timing_create")
         self.h = h
+        if phases is not None:
+            mask = 0
+            for p in phases:
+                mask |= 1 << N.PHASES.index(p)
+            N.check(self.lib.moe_timing_select(self.h, mask), "moe_timing_select")
 
     def read(self) -> Dict[str, float]:
+        """Milliseconds per phase; phases not timed are left out."""
         ms = (ctypes.c_float * N.MOE_N_PHASES)()
         N.check(self.lib.moe_timing_read(self.h, ms), "moe_timing_read")
-        return {name: float(ms[i]) for i, name in enumerate(N.PHASES)}
+        return {name: float(ms[i]) for i, name in enumerate(N.PHASES) if ms[i] >= 0.0}
 
     def close(self):
         if self.h:

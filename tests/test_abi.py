@@ -120,6 +120,7 @@ def test_other_entry_points_reject(lib):
     assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, None, p, p, p, p, p, n.value, None) == 1
     assert lib.moe_grouped_swiglu(1, 4, 64, 128, 10, p, p, p, p, p, p, p, n.value - 1, None) == 3
     assert lib.moe_timing_read(None, None) == 1
+    assert lib.moe_timing_select(None, 1) == 1
     # options: misaligned noise, misaligned metrics, metrics without tokens
     bad_noise = N.MoeRouteOptsC(FAKE + 4, None)
     bad_metrics = N.MoeRouteOptsC(None, FAKE + 4)
