@@ -65,10 +65,18 @@ struct Cfg {
   static_assert(TN % 32 == 0 && TM % 32 == 0, "tile shape");
   static_assert(NBUF >= 2 && NBUF <= 5 && STAGE * NBUF <= 160 * 1024, "LDS");
   static_assert((NBUF - 2) * LPS < 64, "vmcnt range");
-  // XOR key of LDS row `row`: rows of one 128-byte bank window pair up
-  // (SB = 64) so that 8 consecutive rows at one logical chunk hit 8 distinct
-  // bank groups.
-  __device__ static int key(int row) { return (row / (128 / SB)) % CPR; }
+  // XOR key of LDS row `row`. A ds_read_b128 of a fragment reads one logical
+  // chunk of 16 consecutive rows per 16-lane phase; the key makes those 16
+  // reads hit 16 distinct 16-byte bank groups of a 256-byte bank window (and
+  // any 8 consecutive rows 8 distinct groups of a 128-byte window).
+  //   SB = 128: bank group (row * 8 + p) % 16, p = chunk ^ key
+  //   SB = 64 : bank group (row * 4 + p) % 16
+  __device__ static int key(int row) {
+    if constexpr (SB == 128)
+      return (row & 7) ^ ((row >> 3) & 1);
+    else
+      return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  }
   __device__ static int swz(int row, int chunk) { return row * SB + ((chunk ^ key(row)) << 4); }
 };
 
@@ -182,7 +190,9 @@ void k_gemm(GemmLaunch g) {
   // Position of this lane in a 1 KB DMA run: row lane / CPR of the run, LDS
   // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ key(row).
   const int lrow = lane / C::CPR;
-  const int lchunk = (lane % C::CPR) ^ C::key(lrow);
+  // Every run this wave copies starts at an LDS row congruent to wave * RPR
+  // modulo 32 (runs of 4 * RPR rows per wave set), which is all the key reads.
+  const int lchunk = (lane % C::CPR) ^ C::key(wave * C::RPR + lrow);
 
   for (int64_t L = L0 + slot; L < L1; L += per_xcd) {
     // grouped raster: GM row tiles x every column tile
