@@ -8,7 +8,10 @@ itself, an RMS of at most 2^-8/sqrt(3), and a gradient's path crosses at most
 three such roundings, so RMS(err) <= 2^-8 RMS(ref), held for every tensor,
 for the weight gradients of every expert separately (exactly zero for an
 expert without tokens), and per token for dx (2^-6 of the token's RMS, the
-per-row estimate being noisier)."""
+per-row estimate being noisier). The RMS of a few rows' rounding errors
+scatters around its expectation, so an expert with fewer than 32 rows is
+held to 2^-7. A gradient the oracle gives as exactly zero must be exactly
+zero."""
 import numpy as np
 import pytest
 import torch
@@ -25,13 +28,16 @@ BF16_RMS = 2.0 ** -8
 WEIGHT_GRADS = ("dw_gate", "dw_up", "dw_down")
 
 
-def check_grad(cfg, name, got, ref):
+def check_grad(cfg, name, got, ref, rows_per_expert=None):
     g = got.astype(np.float64)
     e = g - ref
     assert np.isfinite(g).all(), f"{cfg.name}: {name} not finite"
     r = rms(ref)
+    if r == 0.0:  # an exactly zero gradient (e.g. a constant combine weight) stays exactly zero
+        assert np.all(g == 0.0), f"{cfg.name}: {name} should be exactly zero, max {np.abs(g).max():.3e}"
+        return
     if cfg.dtype == "f32":
-        err = np.abs(e).max() / max(r, 1e-30)
+        err = np.abs(e).max() / r
         assert err <= TOL_F32, f"{cfg.name}: {name} max|err| / RMS = {err:.3e}"
         return
     assert rms(e) <= BF16_RMS * r, f"{cfg.name}: {name} RMS(err) / RMS = {rms(e) / r:.3e}"
@@ -41,7 +47,9 @@ def check_grad(cfg, name, got, ref):
             if re == 0.0:
                 assert np.all(g[x] == 0.0), f"{cfg.name}: {name}[{x}] nonzero for an expert without tokens"
             else:
-                assert rms(e[x]) <= BF16_RMS * re, f"{cfg.name}: {name}[{x}] RMS(err) / RMS = {rms(e[x]) / re:.3e}"
+                few = rows_per_expert is not None and x < len(rows_per_expert) and rows_per_expert[x] < 32
+                bar = 2.0 * BF16_RMS if few else BF16_RMS
+                assert rms(e[x]) <= bar * re, f"{cfg.name}: {name}[{x}] RMS(err) / RMS = {rms(e[x]) / re:.3e}"
     if name == "dx":
         rt = np.sqrt(np.mean(ref ** 2, axis=1))
         et = np.sqrt(np.mean(e ** 2, axis=1))
@@ -60,6 +68,15 @@ CASES = [
     # enough 256 x 256 weight-gradient tiles (128 experts x 2 x 4 and x 8 x 2)
     # for the wide K-grouped tile
     C("bwd_bf16_wide_tiles", T=1024, d_model=512, n_experts=128, top_k=8, d_ff=1024, zipf_s=1.0),
+    # degenerate shapes: one expert and one slot (constant weight 1, so the
+    # router gradient is exactly zero), a single token (fp32: with one token the
+    # router gradient is four numbers, and the differences of the weight rule
+    # amplify bf16 rounding beyond a per-tensor statistic), and 1024 experts
+    # with most of them empty
+    C("bwd_f32_one_expert", T=65, d_model=64, n_experts=1, top_k=1, d_ff=64, dtype="f32"),
+    C("bwd_f32_one_token", T=1, d_model=128, n_experts=8, top_k=4, d_ff=128, dtype="f32", score="sigmoid",
+      shared=True),
+    C("bwd_bf16_e1024", T=384, d_model=64, n_experts=1024, top_k=8, d_ff=64, bias_range=0.1),
 ]
 COEF = {"bwd_f32_softmax": (1e-3, 1e-3), "bwd_bf16_sigmoid_shared": (1e-3, 1e-3)}
 
@@ -85,8 +102,9 @@ def test_backward_matches_oracle(cfg):
         if r is None:
             continue
         e = got[name].astype(np.float64) - r
-        print(f"  {name:10s} RMS(err)/RMS = {rms(e) / rms(r):.3e}  max|err|/RMS = {np.abs(e).max() / rms(r):.3e}")
-        check_grad(cfg, name, got[name], r)
+        rr = max(rms(r), 1e-300)
+        print(f"  {name:10s} RMS(err)/RMS = {rms(e) / rr:.3e}  max|err|/RMS = {np.abs(e).max() / rr:.3e}")
+        check_grad(cfg, name, got[name], r, np.bincount(idx.ravel(), minlength=cfg.n_experts))
 
 
 def test_backward_repeatable():
