@@ -3,7 +3,8 @@ bench.py times: expert ids, combine weights and counts of every token against
 the oracle's fp32 router (bit-exact ids and counts), the dispatch of every
 (token, slot) pair, and the output on a seeded sample of tokens that the
 oracle computes one by one (plus the ragged tail and the tokens of the least
-loaded expert)."""
+loaded expert); the router metrics of the whole layer and one balance
+controller step from its counts."""
 import gc
 
 import numpy as np
@@ -13,7 +14,8 @@ import torch
 import oracle
 from gpu_util import assert_output, assert_routing, assert_within_envelope, output_envelope, rms_ratio, setup
 from mixture_experts_ffn_02_amd.inputs import CONFIGS
-from mixture_experts_ffn_02_amd.layer import to_device, to_host
+from mixture_experts_ffn_02_amd.layer import bias_update, to_device, to_host
+from test_gpu_training import check_metrics
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -92,3 +94,19 @@ def test_output_on_sampled_tokens(run):
     ratio = rms_ratio(y, o["y"])
     print(f"{cfg.name}: max|err|/RMS = {ratio:.3e} over {tok.size} tokens, worst error/envelope = {worst:.3f}")
     assert_output(cfg, y, o["y"], cfg.name)
+
+
+@pytest.mark.timeout(900)
+def test_metrics_and_controller(run):
+    """Router metrics of the full layer against the oracle's (from its fp32
+    logits and ids), and one balance-controller step from the full counts,
+    bit-exact."""
+    cfg, inp, layer, x, g, r = run
+    m = to_host(layer.route(x, metrics=True)["metrics"])
+    torch.cuda.synchronize()
+    check_metrics(m, oracle.router_metrics(r["logits"], r["idx"], cfg.score), cfg.name)
+    bias = inp["sel_bias"] if inp.get("sel_bias") is not None else np.zeros(cfg.n_experts, np.float32)
+    b_d = to_device(bias.copy())
+    bias_update(to_device(r["counts"]), b_d, 1e-3)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(b_d), oracle.bias_update(r["counts"], bias, 1e-3))
