@@ -245,7 +245,8 @@ moe_status moe_forward_ex(const moe_layer *layer, const void *x, int64_t T, cons
 /* Backward pass (training)                                                */
 /* ---------------------------------------------------------------------- */
 
-/* Gradients written by moe_backward: fp32 DEVICE arrays owned by the caller. */
+/* Gradients written by moe_backward: fp32 DEVICE arrays owned by the caller,
+ * each 16-byte aligned (MOE_ERR_INVALID otherwise). */
 typedef struct moe_grads {
     float *dx;          /* [T, d] */
     float *dw_router;   /* [E, d] */

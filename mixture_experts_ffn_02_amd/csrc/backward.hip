@@ -296,25 +296,36 @@ __device__ int64_t block_scan_1024(int64_t x, int64_t* tmp, int64_t* total) {
 }
 
 constexpr int kKgMaxG = 2048;       // groups of a K-grouped launch, at most
+constexpr int kKgMaxV = 4096;       // chunks (virtual groups) of a K-grouped launch, at most
 constexpr int kKgMaxRaster = 4096;  // raster groups for the XCD balance (more: equal tile counts)
 constexpr int kKgTileCost = 4;      // per-tile prologue and epilogue, in K stages
 
 // K segments of the weight-gradient GEMMs, one block: koffs[e] = sum over
 // groups before e of their row counts rounded up to kp (with no offsets: one
-// segment of kp columns); the tile list holds every (group, m-tile), empty
-// groups included (their gradient is zero).
-// A tile's work is its group's K stages plus kKgTileCost, so groups of
-// unequal size (skewed routing, the shared expert's T rows) give unequal
-// tiles. With xb, the raster order (as the GEMM walks it: raster groups of
-// kGroupM row tiles x ntn column tiles, row tile fastest) is cut into kXcd
-// ranges of about equal work, at whole columns of a raster group.
+// segment of kp columns).
+// Chunks: a group of s stages (ke K elements each) longer than cap stages
+// (cap > 0) is cut into ceil(s / cap) chunks of near-equal stage counts, so
+// that no tile (skewed routing, the shared expert's T rows) runs far longer
+// than the average; vg[v] = (group, first K column, end K column, slot) per
+// chunk, slot -1 for a group's first chunk (which writes the gradient
+// itself) and a partial-buffer slot for the others; red[i] = (group, first
+// slot, slot count) for every cut group, n_red[0] of them, for the ordered
+// reduction that follows the GEMM. The tile list holds every (chunk, m-tile),
+// empty groups included (their gradient is zero).
+// A tile's work is its chunk's K stages plus kKgTileCost. With xb, the
+// raster order (as the GEMM walks it: raster groups of kGroupM row tiles x
+// ntn column tiles, row tile fastest) is cut into kXcd ranges of about equal
+// work, at whole columns of a raster group.
 __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restrict__ offsets, int kp, int mt,
                                                    int32_t* __restrict__ koffs, int2* __restrict__ tiles,
                                                    int32_t* __restrict__ n_tiles, int ntn, int ke,
-                                                   int32_t* __restrict__ xb) {
+                                                   int32_t* __restrict__ xb, int cap, int4* __restrict__ vg,
+                                                   int4* __restrict__ red, int32_t* __restrict__ n_red) {
   __shared__ int32_t ko[kKgMaxG + 1];
+  __shared__ int32_t vst[kKgMaxV];          // K stages of each chunk
   __shared__ int64_t rc[kKgMaxRaster + 1];  // prefix work of the raster groups
   __shared__ int64_t tmp[16];
+  __shared__ int32_t nv_s;
   const int tid = threadIdx.x;
   int64_t carry = 0;
   for (int e0 = 0; e0 < G; e0 += 1024) {  // uniform loop
@@ -331,25 +342,53 @@ __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restr
   if (tid == 0) {
     ko[G] = (int32_t)carry;
     koffs[G] = (int32_t)carry;
-    n_tiles[0] = G * mt;
-  }
-  for (int i = tid; i < G * mt; i += 1024) tiles[i] = make_int2(i / mt, i % mt);
-  if (!xb) return;  // uniform
-  const int64_t m_tiles = (int64_t)G * mt, total = m_tiles * ntn;
-  const int64_t nrg = (m_tiles + kGroupM - 1) / kGroupM;
-  if (nrg > kKgMaxRaster) {  // uniform: equal tile counts
-    if (tid <= kXcd) xb[tid] = (int32_t)((total + kXcd - 1) / kXcd * tid < total ? (total + kXcd - 1) / kXcd * tid : total);
-    return;
   }
   __syncthreads();
+  // chunks of every group
+  int64_t vcarry = 0, scarry = 0, rcarry = 0;
+  for (int e0 = 0; e0 < G; e0 += 1024) {  // uniform loop
+    const int e = e0 + tid;
+    const int st = e < G ? (ko[e + 1] - ko[e]) / ke : 0;
+    const int nch = e < G ? ((cap > 0 && st > cap) ? (st + cap - 1) / cap : 1) : 0;
+    int64_t tv, ts, tr;
+    const int64_t vb = vcarry + block_scan_1024(nch, tmp, &tv);
+    const int64_t sb = scarry + block_scan_1024(nch > 1 ? nch - 1 : 0, tmp, &ts);
+    const int64_t rb = rcarry + block_scan_1024(nch > 1 ? 1 : 0, tmp, &tr);
+    if (e < G) {
+      const int q = (st + nch - 1) / nch;  // stages per chunk
+      for (int c = 0; c < nch; ++c) {
+        const int s0 = c * q < st ? c * q : st, s1 = (c + 1) * q < st ? (c + 1) * q : st;
+        const int64_t vi = vb + c;
+        vg[vi] = make_int4(e, ko[e] + s0 * ke, ko[e] + s1 * ke, c == 0 ? -1 : (int)(sb + c - 1));
+        if (vi < kKgMaxV) vst[vi] = s1 - s0;
+      }
+      if (nch > 1) red[rb] = make_int4(e, (int)sb, nch - 1, 0);
+    }
+    vcarry += tv;
+    scarry += ts;
+    rcarry += tr;
+  }
+  if (tid == 0) {
+    nv_s = (int32_t)vcarry;
+    n_red[0] = (int32_t)rcarry;
+    n_tiles[0] = (int32_t)vcarry * mt;
+  }
+  __syncthreads();
+  const int nv = nv_s;
+  for (int i = tid; i < nv * mt; i += 1024) tiles[i] = make_int2(i / mt, i % mt);
+  if (!xb) return;  // uniform
+  const int64_t m_tiles = (int64_t)nv * mt, total = m_tiles * ntn;
+  const int64_t nrg = (m_tiles + kGroupM - 1) / kGroupM;
+  if (nrg > kKgMaxRaster || nv > kKgMaxV) {  // uniform: equal tile counts
+    const int64_t c = (total + kXcd - 1) / kXcd;
+    if (tid <= kXcd) xb[tid] = (int32_t)(c * tid < total ? c * tid : total);
+    return;
+  }
   // work of one column of raster group r (its row tiles), per thread
   auto col_work = [&](int64_t r) {
     int64_t w = 0;
     const int64_t m1 = (r + 1) * kGroupM < m_tiles ? (r + 1) * kGroupM : m_tiles;
-    for (int64_t m = r * kGroupM; m < m1; ++m) {
-      const int e = (int)(m / mt);
-      w += (ko[e + 1] - ko[e]) / ke + kKgTileCost;
-    }
+    for (int64_t m = r * kGroupM; m < m1; ++m) w += vst[m / mt] + kKgTileCost;
     return w;
   };
   // prefix sums: each thread a contiguous run of raster groups, then the runs
@@ -392,6 +431,23 @@ __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restr
     }
     xb[tid] = (int32_t)L;
   }
+}
+
+// After a chunked K-grouped GEMM: the gradient of every cut group gets its
+// partial sums added, in slot order, to what its first chunk wrote. One
+// thread per 4 columns of one row; blockIdx.y picks the cut group.
+__global__ __launch_bounds__(256) void k_kg_reduce(GemmLaunch g, const int4* __restrict__ red,
+                                                   const int32_t* __restrict__ n_red) {
+  if ((int)blockIdx.y >= n_red[0]) return;  // uniform
+  const int4 r = red[blockIdx.y];
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)g.m_valid * g.N) return;
+  const int mm = (int)(i / g.N), col = (int)(i % g.N);
+  float* dst = kg_out_row(g, r.x, mm) + col;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
+  for (int q = 0; q < r.z; ++q)
+    acc += *reinterpret_cast<const f32x4*>(g.part + ((size_t)(r.y + q) * g.m_rows + mm) * g.N + col);
+  *reinterpret_cast<f32x4*>(dst) = acc;
 }
 
 // Router logit gradients, one thread per token, in fp32: from the
@@ -553,11 +609,20 @@ hipError_t launch_sum_segments(const float* part, int nseg, int64_t seg_stride, 
 }
 
 hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_t* koffs, int2* tiles,
-                           int32_t* n_tiles, hipStream_t s, int ntn, int ke, int32_t* xcd_bounds) {
-  if (G < 1 || G > kKgMaxG || mt < 1) return hipErrorInvalidValue;
-  if (xcd_bounds && (ntn < 1 || ke < 1 || (int64_t)G * mt * ntn > 0x7FFFFFFF)) return hipErrorInvalidValue;
+                           int32_t* n_tiles, int4* vgroups, int cap, int4* red, int32_t* n_red, hipStream_t s, int ntn,
+                           int ke, int32_t* xcd_bounds) {
+  if (G < 1 || G > kKgMaxG || mt < 1 || ke < 1 || !vgroups || !red || !n_red) return hipErrorInvalidValue;
+  if (xcd_bounds && ntn < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kg_setup, dim3(1), dim3(1024), 0, s, G, offsets, kp, mt, koffs, tiles, n_tiles, ntn, ke,
-                     xcd_bounds);
+                     xcd_bounds, cap, vgroups, red, n_red);
+  return hipGetLastError();
+}
+
+hipError_t launch_kg_reduce(const GemmLaunch& g, const int4* red, const int32_t* n_red, int max_red, hipStream_t s) {
+  if (max_red <= 0 || g.m_valid <= 0 || g.N % 4) return hipSuccess;
+  const int64_t n4 = (int64_t)g.m_valid * g.N / 4;
+  hipLaunchKernelGGL(k_kg_reduce, dim3((unsigned)((n4 + 255) / 256), (unsigned)max_red), dim3(256), 0, s, g, red,
+                     n_red);
   return hipGetLastError();
 }
 

@@ -207,11 +207,14 @@ void k_gemm(GemmLaunch g) {
     int64_t row0;
     int rows;
     bool skip = false;
+    int4 chunk_k = make_int4(0, 0, 0, -1);  // K-grouped: (group, first K column, end K column, slot)
     if constexpr (GROUPED) {
       const int2 t = g.tiles[tile_m];
       skip = t.x < 0 || t.x >= g.n_groups || t.y < 0;
       grp = skip ? 0 : t.x;
       if (kg) {
+        chunk_k = g.vgroups[grp];
+        grp = chunk_k.x;
         row0 = (int64_t)t.y * BM;
         const int64_t left = (int64_t)g.m_valid - row0;
         rows = (int)(left < BM ? left : BM);
@@ -231,9 +234,9 @@ void k_gemm(GemmLaunch g) {
     const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a) +
                              (kg ? (size_t)row0 * g.K * sizeof(DT) : (size_t)0);
     const bool xg = grp == g.extra_group;
-    // K range of this tile: the whole K, or the group's columns (K-grouped)
-    const int nk = kg ? (g.koffs[grp + 1] - g.koffs[grp]) / C::KE : nk_all;
-    const int64_t st0 = kg ? (int64_t)g.koffs[grp] / C::KE : 0;  // first K stage of the group
+    // K range of this tile: the whole K, or the chunk's columns (K-grouped)
+    const int nk = kg ? (chunk_k.z - chunk_k.y) / C::KE : nk_all;
+    const int64_t st0 = kg ? (int64_t)chunk_k.y / C::KE : 0;  // first K stage of the chunk
     const unsigned char* B0 = kg ? reinterpret_cast<const unsigned char*>(g.b0) + (size_t)n0 * g.K * sizeof(DT)
                               : xg ? reinterpret_cast<const unsigned char*>(g.bx0)
                                    : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * g.N * kbytes;
@@ -419,19 +422,12 @@ void k_gemm(GemmLaunch g) {
       auto plain_row = [&](void* base, int eb) {
         return [=](int m) { return reinterpret_cast<unsigned char*>(base) + (size_t)(row0 + m) * g.N * eb; };
       };
-      // K-grouped output rows: group grp, row row0 + m of its m_rows
+      // K-grouped output rows: row row0 + m of group grp's m_rows, or of the
+      // chunk's partial-buffer slot
       auto kg_row = [&](int m) {
         const int mm = (int)row0 + m;
-        const bool second = g.m0 > 0 && mm >= g.m0;
-        const int rows0 = g.m0 > 0 ? g.m0 : g.m_rows;
-        unsigned char* base;
-        if (xg)
-          base = reinterpret_cast<unsigned char*>(second ? g.xout1 : g.xout0);
-        else if (second)
-          base = reinterpret_cast<unsigned char*>(g.out1) + (size_t)grp * (g.m_rows - g.m0) * g.N * 4;
-        else
-          base = reinterpret_cast<unsigned char*>(g.out) + (size_t)grp * rows0 * g.N * 4;
-        return base + (size_t)(second ? mm - g.m0 : mm) * g.N * 4;
+        float* p = chunk_k.w >= 0 ? g.part + ((size_t)chunk_k.w * g.m_rows + mm) * g.N : kg_out_row(g, grp, mm);
+        return reinterpret_cast<unsigned char*>(p);
       };
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
@@ -523,6 +519,15 @@ int gemm_kg_bm(int dtype, int m_rows, int n, int groups) {
 // Column tile of a K-grouped launch: 256 with 256-row tiles, else the wider
 // of 128 and 64 that divides n.
 int gemm_kg_bn(int bm, int n) { return bm == 256 ? 256 : (n % 128 == 0 ? 128 : 64); }
+
+// Chunk length: the average K stages per persistent block (one block per CU
+// for 256-row tiles, two otherwise), at least 16, so that a long group's
+// tiles do not outlast the rest of the launch.
+int gemm_kg_cap(int bm, int64_t stages, int mt, int ntn) {
+  const int64_t slots = (int64_t)cu_count() * (bm == 256 ? 1 : 2);
+  const int64_t avg = (stages * mt * ntn + slots - 1) / slots;
+  return (int)(avg < 16 ? 16 : (avg > (1 << 30) ? (1 << 30) : avg));
+}
 
 // gate/up: BN columns of H (gate and up rows staged together); down: BN output
 // columns. The widest tile that divides N. K-grouped launches (weight

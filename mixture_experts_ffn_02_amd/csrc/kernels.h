@@ -86,21 +86,39 @@ struct GemmLaunch {
   // which the backward pass needs
   float* out_g = nullptr;
   float* out_u = nullptr;
-  // K-grouped mode (weight gradients): group e of the tile list reduces over
-  // K columns koffs[e] .. koffs[e+1]-1 (multiples of the K stage) of A (m_rows
-  // rows) and B (N rows), both panelled with K capacity K >= koffs[G] and
-  // panels of BM (A) and BN (B) rows (see panel_offset). Its output is
-  // [m_rows, N] (rows >= m_valid are not stored); rows below m0 go to out +
-  // e*m0*N, the others to out1 + e*(m_rows-m0)*N (m0 = 0: all to out); the
-  // extra group writes to xout0 / xout1 instead. No row gather, no weight
-  // stacking.
+  // K-grouped mode (weight gradients): entry v of the tile list is chunk v,
+  // vgroups[v] = (group e, first K column, end K column, slot), reducing over
+  // those K columns (multiples of the K stage) of A (m_rows rows) and B (N
+  // rows), both panelled with K capacity K and panels of BM (A) and BN (B)
+  // rows (see panel_offset). Its output is [m_rows, N] (rows >= m_valid are
+  // not stored): for slot -1 the gradient of group e (kg_out_row), else
+  // partial buffer `part` + slot*m_rows*N. No row gather, no weight stacking.
+  // koffs marks the mode (the group segments the chunks were cut from).
   const int32_t* koffs = nullptr;
+  const int4* vgroups = nullptr;
+  float* part = nullptr;
   const int32_t* xcd_bounds = nullptr;  // [kXcd + 1] ranges of the raster order per XCD (launch_kg_setup)
   int m_rows = 0, m_valid = 0, m0 = 0;
   void* out1 = nullptr;
   void* xout0 = nullptr;
   void* xout1 = nullptr;
 };
+
+// K-grouped output row mm (of m_rows) of group grp: rows below m0 go to out +
+// grp*m0*N, the others to out1 + grp*(m_rows-m0)*N (m0 = 0: all to out, grp*
+// m_rows*N); the extra group writes to xout0 / xout1 instead. fp32.
+__host__ __device__ inline float* kg_out_row(const GemmLaunch& g, int grp, int mm) {
+  const bool second = g.m0 > 0 && mm >= g.m0;
+  const int rows0 = g.m0 > 0 ? g.m0 : g.m_rows;
+  float* base;
+  if (grp == g.extra_group)
+    base = static_cast<float*>(second ? g.xout1 : g.xout0);
+  else if (second)
+    base = static_cast<float*>(g.out1) + (size_t)grp * (g.m_rows - g.m0) * g.N;
+  else
+    base = static_cast<float*>(g.out) + (size_t)grp * rows0 * g.N;
+  return base + (size_t)(second ? mm - g.m0 : mm) * g.N;
+}
 // Row tile (128 or 256) for `rows` rows in `groups` groups and n output
 // columns; the tile list of a grouped launch must be built with the same value.
 int gemm_bm(int dtype, int64_t rows, int64_t groups, int n);
@@ -137,13 +155,23 @@ hipError_t launch_transpose_groups(int dtype_in, int dtype, const void* in, cons
                                    int panel, int64_t max_cols, void* out, hipStream_t s);
 // out[e][c] = sum over segments s (in order) of part[s][e][c], e < rows_out
 hipError_t launch_sum_segments(const float* part, int nseg, int64_t seg_stride, int64_t n, float* out, hipStream_t s);
-// K segments and tile list of a K-grouped launch: koffs[e] = sum over groups
-// before e of their row counts rounded up to kp (no offsets: kp each); tiles
-// = every (group, m-tile), mt m-tiles a group. With xcd_bounds: the ranges of
-// the launch's raster order (ntn column tiles, kGroupM row tiles a raster
-// group) that give each XCD an equal share of K stages (ke elements each).
+// K segments, chunks and tile list of a K-grouped launch: koffs[e] = sum over
+// groups before e of their row counts rounded up to kp (no offsets: kp each);
+// groups longer than cap stages (ke K elements each; cap <= 0: no cut) are cut
+// into chunks, vgroups[v] as GemmLaunch describes; red / n_red list the cut
+// groups for launch_kg_reduce; tiles = every (chunk, m-tile), mt m-tiles a
+// chunk. With xcd_bounds: the ranges of the launch's raster order (ntn column
+// tiles, kGroupM row tiles a raster group) that give each XCD an equal share
+// of K stages. Sizes: vgroups and red hold G + (total stages) / cap entries.
 hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_t* koffs, int2* tiles,
-                           int32_t* n_tiles, hipStream_t s, int ntn = 0, int ke = 0, int32_t* xcd_bounds = nullptr);
+                           int32_t* n_tiles, int4* vgroups, int cap, int4* red, int32_t* n_red, hipStream_t s,
+                           int ntn = 0, int ke = 1, int32_t* xcd_bounds = nullptr);
+// Adds the partial sums of every cut group (red, n_red[0] of at most max_red)
+// to its gradient in slot order.
+hipError_t launch_kg_reduce(const GemmLaunch& g, const int4* red, const int32_t* n_red, int max_red, hipStream_t s);
+// Work-conserving chunk length (K stages) for a K-grouped launch of row tile
+// bm with mt x ntn tiles per group and at most `stages` K stages in all.
+int gemm_kg_cap(int bm, int64_t stages, int mt, int ntn);
 hipError_t launch_router_bwd(int64_t T, int E, int ep, int k, const float* logits, const int32_t* idx,
                              const float* dtw, const int32_t* counts, int score, int renorm, float z_coef,
                              float aux_coef, float* dl, hipStream_t s);

@@ -277,10 +277,13 @@ struct BwdLayout {
   size_t hist, base, rank, counts, offsets, n_tiles, tiles, row_of, tok_of_row;
   size_t h, g, u, dyb, wrow, dh, dgu, dxp, wdt, wgut;
   size_t koffs, kg_tiles, kg_n, xt, dyt, ht, dgut;
-  size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn, rpart, xb;
+  size_t logits, dtw, dl, dlt, xtr, wrt, dxr, rkoffs, rtiles, rn, rpart, xb, vg, red, nred, part;
   size_t total;
   int64_t nb, rows, gemm_rows, max_tiles, kp, tp, kg_tiles_max, rseg;
   int G, ep, nseg;
+  // weight-gradient launches: row / column tiles, m-tiles per chunk, chunk
+  // length (K stages) and the bound on chunks (virtual groups)
+  int bm_d, bm_gu, bn_d, bn_gu, mt_d, mt_gu, cap_d, cap_gu, vmax;
 };
 
 BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
@@ -310,8 +313,24 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
     o.nseg = (int)((tpad + seg - 1) / seg);
     o.tp = o.nseg * seg;
   }
-  const int64_t mt = (2 * f > d ? 2 * f : d) / 64;  // m-tiles per group, at most
-  o.kg_tiles_max = o.G * mt;
+  // Weight-gradient launches: groups longer than a chunk are cut (at most
+  // stages / cap extra chunks, each with a partial buffer of m_rows x N fp32).
+  const int dt = L->dtype;
+  const int64_t stages = o.kp / (dt == MOE_BF16 ? 64 : 32);
+  o.bm_d = gemm_kg_bm(dt, (int)d, (int)f, o.G);
+  o.bm_gu = gemm_kg_bm(dt, (int)(2 * f), (int)d, o.G);
+  o.bn_d = gemm_kg_bn(o.bm_d, (int)f);
+  o.bn_gu = gemm_kg_bn(o.bm_gu, (int)d);
+  o.mt_d = (int)(d / o.bm_d);
+  o.mt_gu = (int)(2 * f / o.bm_gu);
+  o.cap_d = gemm_kg_cap(o.bm_d, stages, o.mt_d, (int)(f / o.bn_d));
+  o.cap_gu = gemm_kg_cap(o.bm_gu, stages, o.mt_gu, (int)(d / o.bn_gu));
+  const int64_t extra_d = stages / o.cap_d, extra_gu = stages / o.cap_gu;
+  const int64_t vmax = o.G + (extra_d > extra_gu ? extra_d : extra_gu);
+  o.vmax = (int)(vmax > o.nseg ? vmax : o.nseg);
+  const int64_t mt = o.mt_d > o.mt_gu ? o.mt_d : o.mt_gu;
+  o.kg_tiles_max = (int64_t)o.vmax * mt;
+  const int64_t part_floats = (extra_d * d * f > extra_gu * 2 * f * d) ? extra_d * d * f : extra_gu * 2 * f * d;
   size_t p = 0;
   auto take = [&](size_t bytes) {
     const size_t at = p;
@@ -357,6 +376,10 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
   o.rn = take(4);
   o.rpart = o.nseg > 1 ? take(4 * (size_t)o.nseg * o.ep * d) : 0;
   o.xb = take(4 * (kXcd + 1));
+  o.vg = take(sizeof(int4) * (size_t)o.vmax);
+  o.red = take(sizeof(int4) * (size_t)(o.G > o.nseg ? o.G : o.nseg));
+  o.nred = take(4);
+  o.part = part_floats > 0 ? take(4 * (size_t)part_floats) : 0;
   o.total = p;
   return o;
 }
@@ -392,6 +415,10 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   const bool shared = L->d_ff_shared > 0;
   if (shared != (gr->dws_gate && gr->dws_up && gr->dws_down)) return MOE_ERR_INVALID;
   if (T > 0 && (!x || !topk_idx || !topk_w || !dy || !aligned16(x) || !aligned16(dy) || !aligned16(gr->dx)))
+    return MOE_ERR_INVALID;
+  // gradients are written (and chunk sums added) 16 bytes at a time
+  if (!aligned16(gr->dw_router) || !aligned16(gr->dw_gate) || !aligned16(gr->dw_up) || !aligned16(gr->dw_down) ||
+      (shared && (!aligned16(gr->dws_gate) || !aligned16(gr->dws_up) || !aligned16(gr->dws_down))))
     return MOE_ERR_INVALID;
   const BwdLayout lo = make_bwd_layout(L, T);
   if (T > 0 && (!ws || ws_bytes < lo.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
@@ -512,8 +539,11 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   MOE_TRY(launch_transpose(0, 0, L->w_router, wrt, 1, E, lo.ep, d, lo.ep, 0, s)); // [E, d] -> [d, ep]
   int32_t* rkoffs = at<int32_t>(ws, lo.rkoffs);
   // nseg K segments of rseg tokens each
+  int4* vg = at<int4>(ws, lo.vg);
+  int4* red = at<int4>(ws, lo.red);
+  int32_t* nred = at<int32_t>(ws, lo.nred);
   MOE_TRY(launch_kg_setup(lo.nseg, nullptr, (int)lo.rseg, lo.ep / rbm, rkoffs, at<int2>(ws, lo.rtiles),
-                          at<int32_t>(ws, lo.rn), s, d / rbn, 32, at<int32_t>(ws, lo.xb)));
+                          at<int32_t>(ws, lo.rn), vg, 0, red, nred, s, d / rbn, 32, at<int32_t>(ws, lo.xb)));
   GemmLaunch rw{};
   rw.dtype = 0;
   rw.gateup = false;
@@ -529,6 +559,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   rw.max_m_tiles = (int64_t)lo.nseg * (lo.ep / rbm);
   rw.koffs = rkoffs;
   rw.xcd_bounds = at<int32_t>(ws, lo.xb);
+  rw.vgroups = vg;
   rw.m_rows = lo.ep;
   rw.m_valid = E;
   MOE_TRY(launch_gemm(rw, rbm, s));
@@ -551,17 +582,16 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
 
   // 9. weight gradients: per-group K segments of transposed activations
   int32_t* koffs = at<int32_t>(ws, lo.koffs);
-  const int bm_d = gemm_kg_bm(dt, d, f, G), bm_gu = gemm_kg_bm(dt, 2 * f, d, G);
-  const int bn_d = gemm_kg_bn(bm_d, f), bn_gu = gemm_kg_bn(bm_gu, d);
-  const int mt_d = d / bm_d, mt_gu = 2 * f / bm_gu;
+  const int bm_d = lo.bm_d, bm_gu = lo.bm_gu, bn_d = lo.bn_d, bn_gu = lo.bn_gu, mt_d = lo.mt_d, mt_gu = lo.mt_gu;
   unsigned char* xt = at<unsigned char>(ws, lo.xt);
   unsigned char* dyt = at<unsigned char>(ws, lo.dyt);
   unsigned char* ht = at<unsigned char>(ws, lo.ht);
   unsigned char* dgut = at<unsigned char>(ws, lo.dgut);
   const int ke = dt == 1 ? 64 : 32;  // K elements of one stage
   int32_t* xb = at<int32_t>(ws, lo.xb);
-  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_d, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s,
-                          f / bn_d, ke, xb));
+  // chunks of at most cap_d stages (the long groups' partial sums are added in order after the GEMM)
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_d, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), vg,
+                          lo.cap_d, red, nred, s, f / bn_d, ke, xb));
   // per-group zero-padded K segments, panelled for the GEMM that reads them
   // (panels of its row or column tile, K capacity kp >= koffs[G])
   // dY rows are w dy_t, formed here from the fp32 dy (one rounding)
@@ -579,7 +609,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wd.out = gr->dw_down;
   wd.N = f;
   wd.K = (int)lo.kp;  // K capacity of the panels
-  wd.n_groups = G;
+  wd.n_groups = lo.vmax;  // chunks
   wd.extra_group = shared ? E : -1;
   wd.xout0 = gr->dws_down;
   wd.offsets = offsets;
@@ -587,13 +617,16 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wd.n_tiles = at<int32_t>(ws, lo.kg_n);
   wd.max_m_tiles = lo.kg_tiles_max;
   wd.koffs = koffs;
+  wd.vgroups = vg;
+  wd.part = lo.part ? at<float>(ws, lo.part) : nullptr;
   wd.xcd_bounds = xb;
   wd.m_rows = d;
   wd.m_valid = d;
   MOE_TRY(launch_gemm(wd, bm_d, s));
+  MOE_TRY(launch_kg_reduce(wd, red, nred, lo.part ? G : 0, s));
   // dW_gate[e], dW_up[e] [f, d] = [dG_e | dU_e]^T X_e: one launch of 2f rows
-  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_gu, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), s,
-                          d / bn_gu, ke, xb));
+  MOE_TRY(launch_kg_setup(G, offsets, kKPad, mt_gu, koffs, at<int2>(ws, lo.kg_tiles), at<int32_t>(ws, lo.kg_n), vg,
+                          lo.cap_gu, red, nred, s, d / bn_gu, ke, xb));
   GemmLaunch wg = wd;
   wg.a = dgut;
   wg.b0 = xt;
@@ -606,6 +639,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   wg.m_valid = 2 * f;
   wg.m0 = f;
   MOE_TRY(launch_gemm(wg, bm_gu, s));
+  MOE_TRY(launch_kg_reduce(wg, red, nred, lo.part ? G : 0, s));
   return MOE_OK;
 }
 

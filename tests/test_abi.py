@@ -137,6 +137,9 @@ def test_other_entry_points_reject(lib):
     assert lib.moe_backward(ctypes.byref(c), p, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), None, 0, None) == 3
     assert lib.moe_backward(ctypes.byref(c), None, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), p, 1 << 40,
                             None) == 1
+    misaligned = N.MoeGradsC(*([FAKE] * 2 + [FAKE + 4] + [FAKE] * 2 + [None] * 4))
+    assert lib.moe_backward(ctypes.byref(c), p, 10, p, p, p, 0.0, 0.0, ctypes.byref(misaligned), p, 1 << 40,
+                            None) == 1
     sh = layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=128)
     assert lib.moe_backward(ctypes.byref(sh), p, 10, p, p, p, 0.0, 0.0, ctypes.byref(grads), p, 1 << 40, None) == 1
     wide = layer(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, d_ff_shared=192)
