@@ -18,8 +18,8 @@ import torch
 
 import oracle
 from gpu_util import rms, setup
-from mixture_experts_ffn_02_amd.inputs import LayerConfig
-from mixture_experts_ffn_02_amd.layer import to_device, to_host
+from mixture_experts_ffn_02_amd.inputs import LayerConfig, make_layer
+from mixture_experts_ffn_02_amd.layer import MoELayer, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,34 @@ def test_backward_matches_oracle(cfg):
         rr = max(rms(r), 1e-300)
         print(f"  {name:10s} RMS(err)/RMS = {rms(e) / rr:.3e}  max|err|/RMS = {np.abs(e).max() / rr:.3e}")
         check_grad(cfg, name, got[name], r, np.bincount(idx.ravel(), minlength=cfg.n_experts))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_collapsed_router(dtype):
+    """A collapsed router (PR #931, "What to watch"): a +10 selection bias puts
+    expert 0 in slot 0 of every token, so its group holds all T rows and the
+    weight-gradient launches cut it into chunks whose partial sums are added
+    after the GEMM; with a shared expert (another T-row group)."""
+    cfg = LayerConfig(f"bwd_collapse_{dtype}", T=2048, d_model=128, n_experts=8, top_k=2, d_ff=128, dtype=dtype,
+                      score="sigmoid", shared=True, bias_range=0.1)
+    print(f"[case] {cfg.name}", flush=True)
+    inp = make_layer(cfg)
+    inp["sel_bias"] = np.zeros(cfg.n_experts, np.float32)
+    inp["sel_bias"][0] = 10.0
+    layer = MoELayer.from_host(cfg, inp)
+    x = to_device(inp["x"])
+    fw = layer.forward(x)
+    torch.cuda.synchronize()
+    idx, w = to_host(fw["idx"]), to_host(fw["w"])
+    assert np.all(idx[:, 0] == 0)
+    dy = np.random.default_rng(3).standard_normal((cfg.T, cfg.d_model)).astype(np.float32)
+    g = layer.backward(x, fw["idx"], fw["w"], to_device(dy))
+    torch.cuda.synchronize()
+    got = {n: to_host(v) for n, v in g.items()}
+    ref = oracle.backward(inp, idx, w, dy, cfg.score, cfg.renorm, 0.0, 0.0)
+    for name, r in ref.items():
+        if r is not None:
+            check_grad(cfg, name, got[name], r, np.bincount(idx.ravel(), minlength=cfg.n_experts))
 
 
 def test_backward_repeatable():
