@@ -90,8 +90,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
   const int chunk = (nb + R - 1) / R;
   const int b0 = g * chunk, b1 = min(nb, b0 + chunk);
   int s = 0;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) s += hist[(size_t)b * E + e];
+  if (e < E) {
+    // the loads of a thread's blocks are independent: batch them
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = hist[(size_t)(b + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; b < b1; ++b) s += hist[(size_t)b * E + e];
+  }
   part[tid] = s;
   __syncthreads();
   // per expert: inclusive prefix over the block ranges, log2(R) steps
@@ -119,7 +129,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
   }
   if (e < E) {
     int run = cnt[e] + part[tid] - s;  // rows of expert e before block b0
-    for (int b = b0; b < b1; ++b) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = hist[(size_t)(b + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        base[(size_t)(b + q) * E + e] = run;
+        run += v[q];
+      }
+    }
+    for (; b < b1; ++b) {
       base[(size_t)b * E + e] = run;
       run += hist[(size_t)b * E + e];
     }
