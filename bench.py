@@ -142,10 +142,14 @@ def cpu_baseline(cfg, inputs, target_s: float):
     t_small = run(n0)
     n = int(min(cfg.T, max(n0, n0 * target_s / max(t_small, 1e-6))))
     t = run(n) if n > n0 else t_small
-    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": oracle.lib().oracle_num_threads(),
+    reps = 1
+    while t < target_s and reps < 64:  # the whole layer takes less than the target: repeat it
+        t += run(n)
+        reps += 1
+    return {"value": round(n * reps / t, 2), "unit": "tokens/s", "cores": oracle.lib().oracle_num_threads(),
             "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens of the same layer: fp32 router + fp64 experts and combine, "
-                      f"{t:.2f} s"}
+            "sample": f"first {n} of {cfg.T} tokens of the same layer, {reps} run(s): fp32 router + fp64 experts "
+                      f"and combine, {t:.2f} s in all"}
 
 
 def main():
