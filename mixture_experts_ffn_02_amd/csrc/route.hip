@@ -75,14 +75,15 @@ struct RouteShape;
 // every CU. With few experts the block is 16 or 32 tokens and a stage is up
 // to 128 features: the loop over d then has few stages, each of which waits
 // for its loads once (16 experts: one chain per thread and 16-token blocks,
-// two blocks per CU at 8192 tokens, measured faster than 32-token blocks).
-// At 256 experts the stage is 16 features so that two blocks fit in one CU's
-// LDS.
+// two blocks per CU at 8192 tokens, measured faster than 32-token blocks;
+// 128 experts: two tokens per thread, 32-token blocks, measured faster than
+// one or four). At 256 experts the stage is 16 features so that two blocks
+// fit in one CU's LDS.
 ROUTE_SHAPE(8, 1, 1, 128)
 ROUTE_SHAPE(16, 1, 1, 128)
 ROUTE_SHAPE(32, 4, 1, 128)
 ROUTE_SHAPE(64, 8, 1, 64)
-ROUTE_SHAPE(128, 8, 4, 32)
+ROUTE_SHAPE(128, 8, 2, 32)
 ROUTE_SHAPE(256, 8, 8, 16)
 ROUTE_SHAPE(512, 16, 4, 16)
 ROUTE_SHAPE(1024, 16, 4, 8)
