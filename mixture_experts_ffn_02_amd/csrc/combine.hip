@@ -4,7 +4,9 @@
 //   y[t] = sum_{j<k} w[t,j] * Y[row_of[t,j]]  (+ S[t], weight 1, added last)
 // A gather: one wave per token reads its k expert rows and writes its output
 // row once, in fp32, slots in order. No atomics, so the result is the same
-// bits on every run.
+// bits on every run. When the tokens are too few to give every CU work, the
+// row is also split into column ranges over grid.y (each element's sum is
+// unchanged).
 #include "common.h"
 #include "kernels.h"
 
@@ -26,9 +28,11 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const 
   __syncthreads();
   if (!valid) return;
   const int n4 = d >> 2;
+  const int span = (n4 + gridDim.y - 1) / gridDim.y;  // float4 columns of this block
+  const int c0 = blockIdx.y * span, c1 = c0 + span < n4 ? c0 + span : n4;
   const int64_t n_rows = T * k;
   const f32x4* Y = reinterpret_cast<const f32x4*>(y_perm);
-  for (int c = lane; c < n4; c += 64) {
+  for (int c = c0 + lane; c < c1; c += 64) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int r = rows_s[wave][j];
@@ -53,8 +57,14 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const in
                           const float* y_shared, float* y, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (k > 32 || (d & 3)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared,
-                     y);
+  // column ranges of at least 64 float4 (one per lane), enough of them for
+  // about two blocks per CU
+  const int64_t bx = (T + 3) / 4;
+  const int64_t want = (2 * (int64_t)cu_count() + bx - 1) / bx;
+  const int64_t most = ((d >> 2) + 63) / 64;
+  const unsigned by = (unsigned)(want < most ? want : most);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)bx, by > 0 ? by : 1u), dim3(256), 0, s, T, d, k, y_perm, row_of, w,
+                     y_shared, y);
   return hipGetLastError();
 }
 

@@ -33,4 +33,23 @@ struct ElemSize<float> {
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// s_waitcnt with vmcnt = n (other counters left at their maximum): gfx9
+// encoding, vmcnt split over bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4):
+// lane i writes lds_wave + 16 i, where lds_wave is the same for the wave.
+__device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned char* lds_run) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+}
+
 }  // namespace moe

@@ -80,18 +80,6 @@ struct Cfg {
   __device__ static int swz(int row, int chunk) { return row * SB + ((chunk ^ key(row)) << 4); }
 };
 
-// s_waitcnt with vmcnt = n (other counters left at their maximum): gfx9
-// encoding, vmcnt split over bits 3:0 and 15:14.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // One 32 x 32 MFMA tile over the 16 bytes of K that each lane holds: lane l
@@ -148,10 +136,6 @@ __device__ __forceinline__ float to_out<float>(float v) {
   return v;
 }
 
-__device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned char* lds_run) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
-}
 
 // GROUPED: rows come from the tile list over group offsets (routed experts);
 // otherwise one dense group of g.rows rows (the shared expert).
@@ -459,19 +443,6 @@ void k_gemm(GemmLaunch g) {
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
-
 template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF, bool BWD = false>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
@@ -493,6 +464,20 @@ hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
 }
 
 }  // namespace
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 
 // Row tile of a grouped GEMM: 256 rows when groups are long enough to fill
 // such tiles and there are enough of them to give every CU several (the

@@ -6,6 +6,9 @@
 
 namespace moe {
 
+// Compute units of the current device (queried once, 256 if the query fails).
+int cu_count();
+
 // ------------------------------------------------------------------ router
 struct RouteLaunch {
   const void* x;         // [T, d] fp32 or bf16 bits

@@ -342,16 +342,39 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   __syncthreads();
   }
 
-  // softmax normaliser per token: max, then sum of exp over experts ascending
+  // softmax normaliser per token: max, then the sum of exp over experts
+  // ascending. A wave per token: lanes take the exps of experts lane + 64 q,
+  // and the sum runs serially over lanes (readlane), so it adds the terms in
+  // the same order as a single loop over e would.
   auto normalisers = [&]() {
-    for (int tt = tid; tt < TT; tt += 256) {
+    constexpr int QN = (EP + 63) / 64;
+    const int lane = tid & 63;
+    for (int tt = tid >> 6; tt < tt_count; tt += 4) {
       const float* l = lg + tt * (EP + 1);
-      float m = l[0];
-      for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      float v[QN];
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        const int e = lane + 64 * q;
+        v[q] = e < E ? l[e] : -__builtin_inff();
+        m = v[q] > m ? v[q] : m;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(m, off, 64);
+        m = o > m ? o : m;
+      }
       float z = 0.0f;
-      for (int e = 0; e < E; ++e) z += canonical_exp(l[e] - m);
-      tok_m[tt] = m;
-      tok_z[tt] = z;
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        const float ex = lane + 64 * q < E ? canonical_exp(v[q] - m) : 0.0f;
+        const int n = E - 64 * q < 64 ? E - 64 * q : 64;
+        for (int i = 0; i < n; ++i) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), i));
+      }
+      if (lane == 0) {
+        tok_m[tt] = m;
+        tok_z[tt] = z;
+      }
     }
     __syncthreads();
   };
@@ -369,7 +392,8 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
     const bool logit_bias = p.bias_on_logits != 0;
     const bool sigmoid = p.score == 1;
     const float* __restrict__ noise = p.noise;
-    for (int base = 0; base < TT; base += 4 * TPW) {
+    for (int base = 0; base < tt_count; base += 4 * TPW) {
+      if (base + wave * TPW >= tt_count) break;  // this wave's tokens are all padding
       const int tt = base + wave * TPW + gi;
       const float* l = lg + tt * (EP + 1);
       uint64_t key[VPL];
@@ -377,7 +401,7 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
       for (int q = 0; q < VPL; ++q) {
         const int e = li + G * q;
         key[q] = 0ull;
-        if (e < E) {
+        if (e < E && tt < tt_count) {
           float v = l[e];
           if (has_bias) {
             if (logit_bias)
@@ -566,75 +590,195 @@ __global__ __launch_bounds__(256) void k_bias_update(const int32_t* __restrict__
   }
 }
 
-// Gate product alone, for batches too small to fill the GPU with whole-row
-// router blocks: a block owns 16 tokens x 64 experts (thread: 1 token x 4
-// experts), so the grid also spans the experts. Each logit is still one fma
-// chain over features ascending, identical to the fused kernel's.
-constexpr int kLogTT = 16, kLogTE = 64, kLogKC = 32;
-template <typename XT>
+// Gate product alone: logits[t, e] into p.logits, one fma chain per logit
+// over features ascending (the same chains as the fused router). Used where
+// whole-row router blocks would leave CUs idle, and by the backward pass.
+//
+// A block owns TT tokens x TE experts; a thread MT x ME chains. Stages of
+// 64 features stream into a ring of NS LDS buffers by global->LDS DMA, NS-1
+// stages ahead of the fmas, so that with few tokens (short of work per
+// chain) the loads in flight still hide the latency. Stage layout:
+// router-weight rows (16-byte chunks, chunk c of row e at position
+// c ^ ((e / ME) & 15), so that the 16 rows read together sit in distinct
+// banks), then the token rows; every thread issues the same number of DMAs
+// (spare ones fetch a valid address into the slack at the end). bf16 token
+// rows are widened once per stage into an fp32 copy (rows padded by 16 bytes)
+// rather than by every chain that reads them.
+constexpr int kLogKC = 64;
+template <int TT_, int TE_, int MT_, int ME_, int NS_>
+struct LogitShape {
+  static constexpr int TT = TT_, TE = TE_, MT = MT_, ME = ME_, NS = NS_;
+  static constexpr int TGN = TT / MT, EGN = TE / ME;
+  static_assert(TGN * EGN == 256, "256 threads");
+  static_assert(NS >= 2 && NS <= 8, "ring depth");
+  static_assert(EGN <= 64 && 64 % EGN == 0, "a wave spans whole token groups");
+  static constexpr int XP = kLogKC + 4;  // fp32 token-row pitch (floats)
+  template <typename XT>
+  static constexpr int wch() { return TE * kLogKC / 4; }
+  template <typename XT>
+  static constexpr int xch() { return TT * kLogKC * (int)sizeof(XT) / 16; }
+  template <typename XT>
+  static constexpr int loads() { return (wch<XT>() + xch<XT>() + 255) / 256; }  // DMAs per thread per stage
+  template <typename XT>
+  static constexpr int stage_bytes() { return loads<XT>() * 4096; }
+  template <typename XT>
+  static constexpr int widened_bytes() { return sizeof(XT) == 2 ? TT * XP * 4 : 0; }
+  template <typename XT>
+  static constexpr int lds_bytes() { return NS * stage_bytes<XT>() + widened_bytes<XT>(); }
+};
+// few tokens: one chain per thread, 16 x 16 blocks, 8 stages in the ring
+using LogitNarrow = LogitShape<16, 16, 1, 1, 8>;
+// more: 2 x 4 chains, 32 x 64 blocks; many: 4 x 4 chains, 64 x 64 blocks
+// (two blocks per CU fit in LDS with bf16 tokens)
+using LogitMid = LogitShape<32, 64, 2, 4, 3>;
+using LogitWide = LogitShape<64, 64, 4, 4, 2>;
+// at most 16 experts: 4 x 1 chains, 64 x 16 blocks
+using LogitFewE = LogitShape<64, 16, 4, 1, 3>;
+
+template <typename LS, typename XT>
 __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
-  constexpr int V = XLoad<XT>::V;
-  __shared__ __align__(16) float xs[2][kLogKC][kLogTT];
-  __shared__ __align__(16) float ws[2][kLogKC][kLogTE];
-  const int tid = threadIdx.x;
-  const int tg = tid % kLogTT, eg = tid / kLogTT;  // 16 x 16
-  const int64_t t0 = (int64_t)blockIdx.x * kLogTT;
-  const int e0 = blockIdx.y * kLogTE;
+  constexpr int TT = LS::TT, TE = LS::TE, MT = LS::MT, ME = LS::ME, NS = LS::NS, EGN = LS::EGN;
+  constexpr int KC = kLogKC, CPR = KC / 4;  // 16-byte weight chunks per row and stage
+  constexpr int XB = (int)sizeof(XT);
+  constexpr int WCH = LS::template wch<XT>(), XCH = LS::template xch<XT>();
+  constexpr int L = LS::template loads<XT>();
+  constexpr int SBYTES = LS::template stage_bytes<XT>();
+  constexpr int XCPR = KC * XB / 16;  // 16-byte token chunks per row and stage
+  constexpr int XP = LS::XP;
+  __shared__ __align__(16) unsigned char lds_raw[LS::template lds_bytes<XT>()];
+  float* xw = reinterpret_cast<float*>(lds_raw + NS * SBYTES);  // widened bf16 token rows [TT][XP]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int eg = tid % EGN, tg = tid / EGN;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int e0 = blockIdx.y * TE;
   const int d = p.d, E = p.E;
-  const XT* __restrict__ x = reinterpret_cast<const XT*>(p.x);
-  constexpr int XCH = kLogTT * kLogKC / V;  // 16-byte x loads per stage
-  constexpr int WCH = kLogTE * kLogKC / 4;  // 512
-  u32x4 xr = u32x4{0u, 0u, 0u, 0u}, wreg[WCH / 256];
-  auto load = [&](int st) {
-    const int k0 = st * kLogKC;
-    if (tid < XCH) {
-      const int tt = tid / (kLogKC / V), c = tid % (kLogKC / V);
-      xr = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + tt < p.T) xr = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * d + k0 + c * V);
-    }
+  const int64_t T = p.T;
+  const unsigned char* __restrict__ xb = reinterpret_cast<const unsigned char*>(p.x);
+  const unsigned char* __restrict__ wb = reinterpret_cast<const unsigned char*>(p.w_router);
+
+  // global source of this thread's DMA i (feature offset added per stage)
+  const unsigned char* src[L];
 #pragma unroll
-    for (int i = 0; i < WCH / 256; ++i) {
-      const int q = tid + i * 256, e = q / (kLogKC / 4), c = q % (kLogKC / 4);
-      wreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (e0 + e < E) wreg[i] = *reinterpret_cast<const u32x4*>(p.w_router + (size_t)(e0 + e) * d + k0 + c * 4);
+  for (int i = 0; i < L; ++i) {
+    const int q = i * 256 + tid;
+    if (q < WCH) {
+      const int e = q / CPR, c = (q % CPR) ^ ((e / ME) & 15);
+      const int er = e0 + e < E ? e0 + e : E - 1;
+      src[i] = wb + ((size_t)er * d + c * 4) * 4;
+    } else if (q < WCH + XCH) {
+      const int tt = (q - WCH) / XCPR, c = (q - WCH) % XCPR;
+      const int64_t tr = t0 + tt < T ? t0 + tt : T - 1;
+      src[i] = xb + ((size_t)tr * d) * XB + c * 16;
+    } else {
+      src[i] = wb;  // spare: in bounds, lands in the slack
     }
-  };
-  auto store = [&](int buf) {
-    if (tid < XCH) {
-      const int tt = tid / (kLogKC / V), c = tid % (kLogKC / V);
-      float f[V];
-      XLoad<XT>::widen(xr, f);
-#pragma unroll
-      for (int v = 0; v < V; ++v) xs[buf][c * V + v][tt] = f[v];
-    }
-#pragma unroll
-    for (int i = 0; i < WCH / 256; ++i) {
-      const int q = tid + i * 256, e = q / (kLogKC / 4), c = q % (kLogKC / 4);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) ws[buf][c * 4 + v][e] = __uint_as_float(wreg[i][v]);
-    }
-  };
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int nst = d / kLogKC;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load(st + 1);
-    const int b = st & 1;
-#pragma unroll 8
-    for (int kk = 0; kk < kLogKC; ++kk) {
-      const float a = xs[b][kk][tg];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(a, ws[b][kk][eg * 4 + j], acc[j]);
-    }
-    if (st + 1 < nst) store((st + 1) & 1);
-    __syncthreads();
   }
-  if (t0 + tg < p.T) {
+  auto issue = [&](int st) {
+    unsigned char* base = lds_raw + (st % NS) * SBYTES + wave * 1024;
+    const size_t wk = (size_t)st * KC * 4, xk = (size_t)st * KC * XB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e0 + eg * 4 + j < E) p.logits[(t0 + tg) * E + e0 + eg * 4 + j] = acc[j];
+    for (int i = 0; i < L; ++i) {
+      const int q = i * 256 + tid;
+      const size_t off = q < WCH ? wk : (q < WCH + XCH ? xk : 0);
+      lds_dma16(src[i] + off, base + i * 4096);
+    }
+  };
+
+  float acc[MT][ME];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
+  // a wave whose tokens are all past T skips the fmas (it still loads); the
+  // test is on a scalar so that the branch is uniform
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool active = t0 + (int64_t)(wave_s * 64 / EGN) * MT < T;
+
+  const int nst = d / KC;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nst) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    // stage st landed (later stages may still be in flight), and this wave's
+    // LDS reads of the previous stage are done
+    const int ahead = nst - 1 - st < NS - 2 ? nst - 1 - st : NS - 2;
+    if (NS >= 8 && ahead >= 6) wait_vm_lgkm0<(NS >= 8 ? 6 : 0) * L>();
+    else if (NS >= 7 && ahead == 5) wait_vm_lgkm0<(NS >= 7 ? 5 : 0) * L>();
+    else if (NS >= 6 && ahead == 4) wait_vm_lgkm0<(NS >= 6 ? 4 : 0) * L>();
+    else if (NS >= 5 && ahead == 3) wait_vm_lgkm0<(NS >= 5 ? 3 : 0) * L>();
+    else if (NS >= 4 && ahead == 2) wait_vm_lgkm0<(NS >= 4 ? 2 : 0) * L>();
+    else if (NS >= 3 && ahead == 1) wait_vm_lgkm0<L>();
+    else wait_vm_lgkm0<0>();
+    // A bare s_barrier: __syncthreads would also wait for the DMAs still in
+    // flight. The memory clobber keeps the LDS reads below it.
+    asm volatile("s_barrier" ::: "memory");
+    const unsigned char* sb = lds_raw + (st % NS) * SBYTES;
+    const float* xs;  // fp32 token rows of this stage, pitch xp floats
+    int xp;
+    if constexpr (XB == 2) {
+      // widen: 8 features (16 bytes) per item; the previous stage's reads of
+      // xw finished before the barrier above
+      for (int q = tid; q < TT * KC / 8; q += 256) {
+        const int tt = q / (KC / 8), c = q % (KC / 8);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + WCH * 16 + tt * KC * 2 + c * 16);
+        float* o = xw + tt * XP + c * 8;
+        *reinterpret_cast<f32x4*>(o) = f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                                             __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u),
+                                                 __uint_as_float(v[3] << 16), __uint_as_float(v[3] & 0xFFFF0000u)};
+      }
+      wait_vm_lgkm0<63>();  // this wave's LDS writes done (DMAs may stay in flight)
+      asm volatile("s_barrier" ::: "memory");
+      xs = xw;
+      xp = XP;
+    } else {
+      xs = reinterpret_cast<const float*>(sb + WCH * 16);
+      xp = KC;
+    }
+    if (st + NS - 1 < nst) issue(st + NS - 1);  // into the buffer of stage st-1
+    if (active) {
+      // chunks in groups of CG, the LDS reads of group g+1 issued before the
+      // fmas of group g (the chains still take the features in order)
+      constexpr int CG = (MT + ME) <= 2 ? 8 : 2;
+      f32x4 a[2][CG][MT], b[2][CG][ME];
+      auto read = [&](int h, int c0) {
+#pragma unroll
+        for (int cc = 0; cc < CG; ++cc) {
+          const int c = c0 + cc;
+#pragma unroll
+          for (int i = 0; i < MT; ++i) a[h][cc][i] = *reinterpret_cast<const f32x4*>(xs + (tg * MT + i) * xp + c * 4);
+#pragma unroll
+          for (int j = 0; j < ME; ++j) {
+            const int e = eg * ME + j;
+            b[h][cc][j] = *reinterpret_cast<const f32x4*>(sb + (e * CPR + (c ^ ((e / ME) & 15))) * 16);
+          }
+        }
+      };
+      read(0, 0);
+#pragma unroll
+      for (int g = 0; g < CPR / CG; ++g) {
+        if (g + 1 < CPR / CG) read((g + 1) & 1, (g + 1) * CG);
+#pragma unroll
+        for (int cc = 0; cc < CG; ++cc)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+              for (int j = 0; j < ME; ++j)
+                acc[i][j] = __builtin_fmaf(a[g & 1][cc][i][u], b[g & 1][cc][j][u], acc[i][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t t = t0 + tg * MT + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < ME; ++j) {
+      const int e = e0 + eg * ME + j;
+      if (e < E) p.logits[t * E + e] = acc[i][j];
+    }
   }
 }
 
@@ -662,16 +806,22 @@ hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLau
   return hipGetLastError();
 }
 
-int cu_count_route() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    n = (hipGetDevice(&dev) == hipSuccess &&
-         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            ? v
-            : 256;
-  }
-  return n;
+// Logits kernel shape for a batch: at most 16 experts, 64 x 16 blocks;
+// otherwise one chain per thread while 32 x 64 blocks would not give every CU
+// one, 32 x 64 blocks while 64 x 64 ones would not give every CU two, else
+// 64 x 64.
+template <typename LS, typename XT>
+hipError_t launch_logits_shape(const RouteLaunch& a, hipStream_t s) {
+  const dim3 g((unsigned)((a.T + LS::TT - 1) / LS::TT), (unsigned)((a.E + LS::TE - 1) / LS::TE));
+  return launch_k(k_logits<LS, XT>, g, 0, s, a);
+}
+template <typename XT>
+hipError_t launch_logits_t(const RouteLaunch& a, hipStream_t s) {
+  const int64_t cu = cu_count(), et = (a.E + 63) / 64;
+  if (a.E <= 16) return launch_logits_shape<LogitFewE, XT>(a, s);
+  if ((a.T + 31) / 32 * et < cu) return launch_logits_shape<LogitNarrow, XT>(a, s);
+  if ((a.T + 63) / 64 * et < 2 * cu) return launch_logits_shape<LogitMid, XT>(a, s);
+  return launch_logits_shape<LogitWide, XT>(a, s);
 }
 
 template <int EP>
@@ -679,13 +829,13 @@ hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   using S = RouteShape<EP>;
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
-  if (a.d % 64 || a.d % kLogKC) return hipErrorInvalidValue;  // stages of min(KC, 64) features
-  // Split path when whole-row blocks would leave CUs idle and the experts are
-  // many: logits first (grid over tokens and experts), then the selection.
-  const bool split = a.logits != nullptr && a.E >= 64 && 4 * nb < cu_count_route();
+  if (a.d % 64) return hipErrorInvalidValue;  // stages of 64 features (or a multiple)
+  // Split path when whole-row blocks would not give every CU two and the
+  // experts are many: logits first (grid over tokens and experts), then the
+  // selection.
+  const bool split = a.logits != nullptr && a.E >= 64 && nb < 2 * (int64_t)cu_count();
   if (split) {
-    const dim3 g((unsigned)((a.T + kLogTT - 1) / kLogTT), (unsigned)((a.E + kLogTE - 1) / kLogTE));
-    hipError_t e = a.dtype == 1 ? launch_k(k_logits<uint16_t>, g, 0, s, a) : launch_k(k_logits<float>, g, 0, s, a);
+    hipError_t e = a.dtype == 1 ? launch_logits_t<uint16_t>(a, s) : launch_logits_t<float>(a, s);
     if (e != hipSuccess) return e;
     return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, true>, dim3((unsigned)nb), lds, s, a)
                         : launch_k(k_route<EP, float, true>, dim3((unsigned)nb), lds, s, a);
@@ -758,9 +908,8 @@ hipError_t launch_bias_update(const int32_t* counts, int E, float rate, float* b
 
 hipError_t launch_logits(const RouteLaunch& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (a.d % kLogKC || !a.logits) return hipErrorInvalidValue;
-  const dim3 g((unsigned)((a.T + kLogTT - 1) / kLogTT), (unsigned)((a.E + kLogTE - 1) / kLogTE));
-  return a.dtype == 1 ? launch_k(k_logits<uint16_t>, g, 0, s, a) : launch_k(k_logits<float>, g, 0, s, a);
+  if (a.d % kLogKC || !a.logits || a.E <= 0) return hipErrorInvalidValue;
+  return a.dtype == 1 ? launch_logits_t<uint16_t>(a, s) : launch_logits_t<float>(a, s);
 }
 
 int hist_tokens_per_block() { return kHistTT; }

@@ -36,9 +36,17 @@ CASES = [
     C("k_equals_E", T=200, d_model=64, n_experts=4, top_k=4, d_ff=64, score="sigmoid"),
     C("single_token", T=1, d_model=64, n_experts=16, top_k=4, d_ff=128, shared=True),
     # enough tokens for the fused router path at 64, 512 and 1024 experts
-    C("fused_router_e64", T=4100, d_model=64, n_experts=64, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
-    C("fused_router_e512", T=2050, d_model=64, n_experts=512, top_k=8, d_ff=64),
-    C("fused_router_e1024", T=1030, d_model=64, n_experts=1024, top_k=4, d_ff=64, bias_range=0.01),
+    # (two whole-row router blocks per CU of a 256-CU part)
+    C("fused_router_e64", T=16400, d_model=64, n_experts=64, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
+    C("fused_router_e512", T=16400, d_model=64, n_experts=512, top_k=8, d_ff=64),
+    C("fused_router_e1024", T=8200, d_model=64, n_experts=1024, top_k=4, d_ff=64, bias_range=0.01),
+    # split path, logits kernel with one chain per thread: ragged tokens and
+    # experts, ten 64-feature stages (the 8-deep ring wraps)
+    C("split_narrow_ring", T=37, d_model=640, n_experts=80, top_k=6, d_ff=64, score="sigmoid", bias_range=0.2),
+    # split path, logits kernel with 2 x 4 chains per thread (bf16), then with
+    # 4 x 4 (fp32 tokens)
+    C("split_mid_ring", T=4100, d_model=256, n_experts=256, top_k=8, d_ff=64),
+    C("split_wide_f32", T=8200, d_model=192, n_experts=256, top_k=4, d_ff=64, dtype="f32", bias_range=0.05),
 ]
 
 
