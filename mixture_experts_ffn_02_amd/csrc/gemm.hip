@@ -486,6 +486,14 @@ int cu_count() {
 int gemm_bm(int dtype, int64_t rows, int64_t groups, int n) {
   if (dtype != 1 || groups <= 0) return 128;
   const int64_t avg = rows / groups;
+  // Few rows per group (small batches, many experts): the weights dominate
+  // the traffic, and 64-row tiles with wider weight tiles stage half as many
+  // padding rows per weight byte, as long as their tiles still give every
+  // block slot of the persistent grid one (else more, narrower tiles win;
+  // at most `rows` groups hold rows).
+  const int64_t busy = groups < rows ? groups : rows;
+  const int64_t tiles64 = busy * (n % 128 == 0 ? n / 128 : n / 64);
+  if (avg <= 64 && tiles64 >= 2 * (int64_t)cu_count()) return 64;
   const int64_t tiles256 = (rows / 256) * (n / 128);
   return (avg >= 768 && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
 }
@@ -534,9 +542,13 @@ hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
       return wide ? launch_t<float, false, 128, 128, 128, 2, true>(g, s) : launch_t<float, false, 128, 64, 128, 2, true>(g, s);
     return wide ? launch_t<float, false, 64, 128, 128, 2, true>(g, s) : launch_t<float, false, 64, 64, 128, 2, true>(g, s);
   }
+  if (bm == 64 && (g.dtype != 1 || g.koffs)) return hipErrorInvalidValue;
   if (g.out_g) {  // gate/up that also stores the pre-activations (backward recompute)
     if (!g.gateup) return hipErrorInvalidValue;
     if (g.dtype == 1) {
+      if (bm == 64)
+        return g.N % 128 == 0 ? launch_t<uint16_t, true, 64, 128, 128, 2, true>(g, s)
+                              : launch_t<uint16_t, true, 64, 64, 128, 2, true>(g, s);
       if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2, true>(g, s);
       if (bm == 256) return launch_t<uint16_t, true, 256, 64, 128, 2, true>(g, s);
       return launch_t<uint16_t, true, 128, 64, 128, 2, true>(g, s);
@@ -544,6 +556,14 @@ hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
     return launch_t<float, true, 128, 64, 128, 2, true>(g, s);
   }
   if (g.dtype == 1) {
+    if (bm == 64) {
+      if (g.gateup)
+        return g.N % 128 == 0 ? launch_t<uint16_t, true, 64, 128, 128, 2>(g, s)
+                              : launch_t<uint16_t, true, 64, 64, 128, 2>(g, s);
+      if (g.N % 256 == 0) return launch_t<uint16_t, false, 64, 256, 128, 2>(g, s);
+      if (g.N % 128 == 0) return launch_t<uint16_t, false, 64, 128, 128, 2>(g, s);
+      return launch_t<uint16_t, false, 64, 64, 128, 2>(g, s);
+    }
     if (g.gateup) {
       if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2>(g, s);
       if (bm == 256) return launch_t<uint16_t, true, 256, 64, 128, 2>(g, s);

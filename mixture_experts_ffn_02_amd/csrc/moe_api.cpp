@@ -72,7 +72,7 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   o.nb = (T + tpb - 1) / tpb;
   const bool merged = shared_as_group(L, T);
   o.gemm_rows = rows + (merged ? T : 0);
-  o.max_tiles = (o.gemm_rows + 127) / 128 + E + 1;  // bound for the smallest row tile
+  o.max_tiles = (o.gemm_rows + kMinTileRows - 1) / kMinTileRows + E + 1;  // bound for the smallest row tile
   size_t p = 0;
   auto take = [&](size_t bytes) {
     const size_t at = p;
@@ -296,7 +296,7 @@ BwdLayout make_bwd_layout(const moe_layer* L, int64_t T) {
   o.gemm_rows = o.rows + (shared ? T : 0);
   const int64_t tpb = hist_tokens_per_block();
   o.nb = (T + tpb - 1) / tpb;
-  o.max_tiles = (o.gemm_rows + 127) / 128 + o.G;
+  o.max_tiles = (o.gemm_rows + kMinTileRows - 1) / kMinTileRows + o.G;
   o.kp = (o.gemm_rows + (int64_t)kKPad * o.G + kKPad - 1) / kKPad * kKPad;  // bound on the padded K columns
   o.ep = (int)((E + 127) / 128 * 128);
   // The router weight gradient dl^T x has few output tiles: it is split into
@@ -742,7 +742,7 @@ moe_status moe_grouped_swiglu_workspace_size(int32_t dtype, int32_t n_groups, in
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d_in % 64 || d_ff % 64) return MOE_ERR_UNSUPPORTED;
   if (rows > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
-  const int64_t max_tiles = (rows + 127) / 128 + n_groups;
+  const int64_t max_tiles = (rows + kMinTileRows - 1) / kMinTileRows + n_groups;
   size_t p = align_up(sizeof(int32_t));
   p += align_up(sizeof(int2) * (size_t)max_tiles);
   p += align_up((size_t)elem_bytes(dtype) * (size_t)rows * (size_t)d_ff);
@@ -764,7 +764,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const int bm = gemm_bm(dtype, rows, n_groups, d_ff);
-  const int64_t max_tiles = (rows + 127) / 128 + n_groups;
+  const int64_t max_tiles = (rows + kMinTileRows - 1) / kMinTileRows + n_groups;
   int32_t* n_tiles = at<int32_t>(ws, 0);
   int2* tiles = at<int2>(ws, align_up(sizeof(int32_t)));
   void* h = at<void>(ws, align_up(sizeof(int32_t)) + align_up(sizeof(int2) * (size_t)max_tiles));

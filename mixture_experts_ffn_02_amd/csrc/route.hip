@@ -604,19 +604,20 @@ __global__ __launch_bounds__(256) void k_bias_update(const int32_t* __restrict__
 // (spare ones fetch a valid address into the slack at the end). bf16 token
 // rows are widened once per stage into an fp32 copy (rows padded by 16 bytes)
 // rather than by every chain that reads them.
-constexpr int kLogKC = 64;
-template <int TT_, int TE_, int MT_, int ME_, int NS_>
+constexpr int kLogKC = 64;  // d is a multiple of this
+template <int TT_, int TE_, int MT_, int ME_, int NS_, int KC_ = kLogKC>
 struct LogitShape {
-  static constexpr int TT = TT_, TE = TE_, MT = MT_, ME = ME_, NS = NS_;
+  static constexpr int TT = TT_, TE = TE_, MT = MT_, ME = ME_, NS = NS_, KC = KC_;
   static constexpr int TGN = TT / MT, EGN = TE / ME;
   static_assert(TGN * EGN == 256, "256 threads");
   static_assert(NS >= 2 && NS <= 8, "ring depth");
   static_assert(EGN <= 64 && 64 % EGN == 0, "a wave spans whole token groups");
-  static constexpr int XP = kLogKC + 4;  // fp32 token-row pitch (floats)
+  static_assert(TE * KC / 4 >= 256, "the first DMA of every thread is a weight chunk");
+  static constexpr int XP = KC + 4;  // fp32 token-row pitch (floats)
   template <typename XT>
-  static constexpr int wch() { return TE * kLogKC / 4; }
+  static constexpr int wch() { return TE * KC / 4; }
   template <typename XT>
-  static constexpr int xch() { return TT * kLogKC * (int)sizeof(XT) / 16; }
+  static constexpr int xch() { return TT * KC * (int)sizeof(XT) / 16; }
   template <typename XT>
   static constexpr int loads() { return (wch<XT>() + xch<XT>() + 255) / 256; }  // DMAs per thread per stage
   template <typename XT>
@@ -626,8 +627,11 @@ struct LogitShape {
   template <typename XT>
   static constexpr int lds_bytes() { return NS * stage_bytes<XT>() + widened_bytes<XT>(); }
 };
-// few tokens: one chain per thread, 16 x 16 blocks, 8 stages in the ring
-using LogitNarrow = LogitShape<16, 16, 1, 1, 8>;
+// few tokens: one chain per thread, 16 x 16 blocks, stages of 128 features
+// five deep in the ring (64 features eight deep where d is not a multiple of
+// 128)
+using LogitNarrow = LogitShape<16, 16, 1, 1, 5, 128>;
+using LogitNarrow64 = LogitShape<16, 16, 1, 1, 8>;
 // more: 2 x 4 chains, 32 x 64 blocks; many: 4 x 4 chains, 64 x 64 blocks
 // (two blocks per CU fit in LDS with bf16 tokens)
 using LogitMid = LogitShape<32, 64, 2, 4, 3>;
@@ -638,7 +642,7 @@ using LogitFewE = LogitShape<64, 16, 4, 1, 3>;
 template <typename LS, typename XT>
 __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
   constexpr int TT = LS::TT, TE = LS::TE, MT = LS::MT, ME = LS::ME, NS = LS::NS, EGN = LS::EGN;
-  constexpr int KC = kLogKC, CPR = KC / 4;  // 16-byte weight chunks per row and stage
+  constexpr int KC = LS::KC, CPR = KC / 4;  // 16-byte weight chunks per row and stage
   constexpr int XB = (int)sizeof(XT);
   constexpr int WCH = LS::template wch<XT>(), XCH = LS::template xch<XT>();
   constexpr int L = LS::template loads<XT>();
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
       const int64_t tr = t0 + tt < T ? t0 + tt : T - 1;
       src[i] = xb + ((size_t)tr * d) * XB + c * 16;
     } else {
-      src[i] = wb;  // spare: in bounds, lands in the slack
+      src[i] = src[0];  // spare: a copy of this thread's first weight chunk, into the slack
     }
   }
   auto issue = [&](int st) {
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int q = i * 256 + tid;
-      const size_t off = q < WCH ? wk : (q < WCH + XCH ? xk : 0);
+      const size_t off = (q < WCH || q >= WCH + XCH) ? wk : xk;
       lds_dma16(src[i] + off, base + i * 4096);
     }
   };
@@ -819,7 +823,8 @@ template <typename XT>
 hipError_t launch_logits_t(const RouteLaunch& a, hipStream_t s) {
   const int64_t cu = cu_count(), et = (a.E + 63) / 64;
   if (a.E <= 16) return launch_logits_shape<LogitFewE, XT>(a, s);
-  if ((a.T + 31) / 32 * et < cu) return launch_logits_shape<LogitNarrow, XT>(a, s);
+  if ((a.T + 31) / 32 * et < cu)
+    return a.d % 128 == 0 ? launch_logits_shape<LogitNarrow, XT>(a, s) : launch_logits_shape<LogitNarrow64, XT>(a, s);
   if ((a.T + 63) / 64 * et < 2 * cu) return launch_logits_shape<LogitMid, XT>(a, s);
   return launch_logits_shape<LogitWide, XT>(a, s);
 }

@@ -35,14 +35,20 @@ CASES = [
     C("one_expert", T=130, d_model=64, n_experts=1, top_k=1, d_ff=64),
     C("k_equals_E", T=200, d_model=64, n_experts=4, top_k=4, d_ff=64, score="sigmoid"),
     C("single_token", T=1, d_model=64, n_experts=16, top_k=4, d_ff=128, shared=True),
+    # a few rows per expert over many experts: 64-row tiles, 64 x 128 gate/up
+    # and 64 x 256 down weight tiles, the shared expert as one more group
+    C("tiles64_e512_shared", T=700, d_model=256, n_experts=512, top_k=4, d_ff=128, score="sigmoid", shared=True,
+      bias_range=0.1),
     # enough tokens for the fused router path at 64, 512 and 1024 experts
     # (two whole-row router blocks per CU of a 256-CU part)
     C("fused_router_e64", T=16400, d_model=64, n_experts=64, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
     C("fused_router_e512", T=16400, d_model=64, n_experts=512, top_k=8, d_ff=64),
     C("fused_router_e1024", T=8200, d_model=64, n_experts=1024, top_k=4, d_ff=64, bias_range=0.01),
     # split path, logits kernel with one chain per thread: ragged tokens and
-    # experts, ten 64-feature stages (the 8-deep ring wraps)
-    C("split_narrow_ring", T=37, d_model=640, n_experts=80, top_k=6, d_ff=64, score="sigmoid", bias_range=0.2),
+    # experts, eleven 128-feature stages (the 5-deep ring wraps), then nine
+    # 64-feature stages (d not a multiple of 128; the 8-deep ring wraps)
+    C("split_narrow_ring", T=37, d_model=1408, n_experts=80, top_k=6, d_ff=64, score="sigmoid", bias_range=0.2),
+    C("split_narrow_ring64", T=21, d_model=576, n_experts=64, top_k=4, d_ff=64),
     # split path, logits kernel with 2 x 4 chains per thread (bf16), then with
     # 4 x 4 (fp32 tokens)
     C("split_mid_ring", T=4100, d_model=256, n_experts=256, top_k=8, d_ff=64),
