@@ -835,10 +835,13 @@ hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
   if (a.d % 64) return hipErrorInvalidValue;  // stages of 64 features (or a multiple)
-  // Split path when whole-row blocks would not give every CU two and the
-  // experts are many: logits first (grid over tokens and experts), then the
+  // Split path when the experts are many and whole-row blocks would not give
+  // every CU two (four for shapes with at most 16 chains per thread, whose
+  // fused gate product measured slower than the logits kernel's: 128 experts
+  // at 512 blocks), logits first (grid over tokens and experts), then the
   // selection.
-  const bool split = a.logits != nullptr && a.E >= 64 && nb < 2 * (int64_t)cu_count();
+  const int64_t per_cu = S::ME * S::MT >= 32 ? 2 : 4;
+  const bool split = a.logits != nullptr && a.E >= 64 && nb < per_cu * (int64_t)cu_count();
   if (split) {
     hipError_t e = a.dtype == 1 ? launch_logits_t<uint16_t>(a, s) : launch_logits_t<float>(a, s);
     if (e != hipSuccess) return e;

@@ -39,9 +39,11 @@ CASES = [
     # and 64 x 256 down weight tiles, the shared expert as one more group
     C("tiles64_e512_shared", T=700, d_model=256, n_experts=512, top_k=4, d_ff=128, score="sigmoid", shared=True,
       bias_range=0.1),
-    # enough tokens for the fused router path at 64, 512 and 1024 experts
-    # (two whole-row router blocks per CU of a 256-CU part)
-    C("fused_router_e64", T=16400, d_model=64, n_experts=64, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
+    # enough tokens for the fused router path at 64, 128, 512 and 1024
+    # experts (four whole-row router blocks per CU of a 256-CU part at 64 and
+    # 128 experts, two at 512 and 1024)
+    C("fused_router_e64", T=33000, d_model=64, n_experts=64, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
+    C("fused_router_e128", T=32800, d_model=64, n_experts=128, top_k=8, d_ff=64, zipf_s=1.1),
     C("fused_router_e512", T=16400, d_model=64, n_experts=512, top_k=8, d_ff=64),
     C("fused_router_e1024", T=8200, d_model=64, n_experts=1024, top_k=4, d_ff=64, bias_range=0.01),
     # split path, logits kernel with one chain per thread: ragged tokens and
