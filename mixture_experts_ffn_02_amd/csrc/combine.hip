@@ -3,7 +3,8 @@
 // one weighted sum).
 //   y[t] = sum_{j<k} w[t,j] * Y[row_of[t,j]]  (+ S[t], weight 1, added last)
 // A gather: one wave per token reads its k expert rows and writes its output
-// row once, in fp32, slots in order. No atomics, so the result is the same
+// row once, in fp32, slots in order (each lane keeps up to eight row loads in
+// flight). No atomics, so the result is the same
 // bits on every run. When the tokens are too few to give every CU work, the
 // row is also split into column ranges over grid.y (each element's sum is
 // unchanged).
@@ -13,6 +14,7 @@
 namespace moe {
 namespace {
 
+template <int KG>
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const float* __restrict__ y_perm,
                                                  const int32_t* __restrict__ row_of, const float* __restrict__ w,
                                                  const float* __restrict__ y_shared, float* __restrict__ y) {
@@ -34,13 +36,25 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const 
   const f32x4* Y = reinterpret_cast<const f32x4*>(y_perm);
   for (int c = c0 + lane; c < c1; c += 64) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = rows_s[wave][j];
-      if (r < 0 || r >= n_rows) continue;  // invalid row ids contribute nothing
-      const f32x4 v = Y[(size_t)r * n4 + c];
-      const float wj = w_s[wave][j];
+    // slots in groups of KG: the group's loads are issued together (a slot
+    // past k or an invalid row id reads row 0 and contributes nothing), then
+    // added in slot order
+    for (int j0 = 0; j0 < k; j0 += KG) {
+      f32x4 v[KG];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wj, v[q], acc[q]);
+      for (int q = 0; q < KG; ++q) {
+        const int r = j0 + q < k ? rows_s[wave][j0 + q] : -1;
+        const int rr = (r >= 0 && r < n_rows) ? r : 0;
+        v[q] = Y[(size_t)rr * n4 + c];
+      }
+#pragma unroll
+      for (int q = 0; q < KG; ++q) {
+        const int r = j0 + q < k ? rows_s[wave][j0 + q] : -1;
+        if (r < 0 || r >= n_rows) continue;  // invalid row ids contribute nothing
+        const float wj = w_s[wave][j0 + q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wj, v[q][e], acc[e]);
+      }
     }
     if (y_shared) {
       const f32x4 sv = reinterpret_cast<const f32x4*>(y_shared)[(size_t)t * n4 + c];
@@ -63,8 +77,16 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* y_perm, const in
   const int64_t want = (2 * (int64_t)cu_count() + bx - 1) / bx;
   const int64_t most = ((d >> 2) + 63) / 64;
   const unsigned by = (unsigned)(want < most ? want : most);
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)bx, by > 0 ? by : 1u), dim3(256), 0, s, T, d, k, y_perm, row_of, w,
-                     y_shared, y);
+  const dim3 grid((unsigned)bx, by > 0 ? by : 1u);
+  // slot groups of 1, 2, 4 or 8 loads in flight per lane
+  if (k >= 8)
+    hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared, y);
+  else if (k >= 4)
+    hipLaunchKernelGGL(k_combine<4>, grid, dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared, y);
+  else if (k >= 2)
+    hipLaunchKernelGGL(k_combine<2>, grid, dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared, y);
+  else
+    hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, s, T, d, k, y_perm, row_of, w, y_shared, y);
   return hipGetLastError();
 }
 
