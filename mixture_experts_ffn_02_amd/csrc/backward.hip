@@ -450,72 +450,122 @@ __global__ __launch_bounds__(256) void k_kg_reduce(GemmLaunch g, const int4* __r
   *reinterpret_cast<f32x4*>(dst) = acc;
 }
 
-// Router logit gradients, one thread per token, in fp32: from the
-// combine-weight gradients through the forward's weight rule, plus the
-// z-loss (2 lse softmax / T) and aux-loss (E/T f_e dscore_e) terms with the
-// caller's coefficients; written to dl [T, ep] (zero past E).
+// Router logit gradients in fp32, one wave per token and a lane per expert
+// (experts lane + 64 q): from the combine-weight gradients through the
+// forward's weight rule, plus the z-loss (2 lse softmax / T) and aux-loss
+// (E/T f_e dscore_e) terms with the caller's coefficients; written to
+// dl [T, ep] (zero past E). Sums over experts are wave reductions in a fixed
+// shuffle order, sums over slots run in slot order, so the result is the
+// same bits on every call.
+template <int QN>
 __global__ __launch_bounds__(256) void k_router_bwd(int64_t T, int E, int ep, int k, const float* __restrict__ logits,
                                                     const int32_t* __restrict__ idx, const float* __restrict__ dtw,
                                                     const int32_t* __restrict__ counts, int score, int renorm,
                                                     float z_coef, float aux_coef, float* __restrict__ dl) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
   const float* l = logits + t * E;
-  float* o = dl + t * ep;
   const int32_t* id = idx + t * k;
   const float* g = dtw + t * k;
-  float m = l[0];
-  for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
-  float z = 0.0f;
-  for (int e = 0; e < E; ++e) z += expf(l[e] - m);
+  auto wave_sum = [](float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+  };
+  float v[QN], o[QN];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < E ? l[e] : -__builtin_inff();
+    m = v[q] > m ? v[q] : m;
+    o[q] = 0.0f;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float y = __shfl_xor(m, off, 64);
+    m = y > m ? y : m;
+  }
+  float p[QN];  // softmax over all experts
+  float zl = 0.0f;
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    p[q] = lane + 64 * q < E ? expf(v[q] - m) : 0.0f;
+    zl += p[q];
+  }
+  const float z = wave_sum(zl);
   const float lse = m + logf(z);
-  for (int e = 0; e < ep; ++e) o[e] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < QN; ++q) p[q] = p[q] / z;
+  // add `term` to the logit gradient of expert e (its owner lane)
+  auto add_to = [&](int e, float term) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q)
+      if (e == lane + 64 * q) o[q] += term;
+  };
   if (score == 0 && renorm) {
     float mk = l[id[0]];
     for (int j = 1; j < k; ++j) mk = l[id[j]] > mk ? l[id[j]] : mk;
     float zk = 0.0f, dot = 0.0f;
     for (int j = 0; j < k; ++j) zk += expf(l[id[j]] - mk);
     for (int j = 0; j < k; ++j) dot += expf(l[id[j]] - mk) / zk * g[j];
-    for (int j = 0; j < k; ++j) o[id[j]] += expf(l[id[j]] - mk) / zk * (g[j] - dot);
+    for (int j = 0; j < k; ++j) add_to(id[j], expf(l[id[j]] - mk) / zk * (g[j] - dot));
   } else if (score == 0) {
     float dot = 0.0f;
     for (int j = 0; j < k; ++j) dot += expf(l[id[j]] - m) / z * g[j];
-    for (int e = 0; e < E; ++e) o[e] -= expf(l[e] - m) / z * dot;
-    for (int j = 0; j < k; ++j) o[id[j]] += expf(l[id[j]] - m) / z * g[j];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) o[q] -= p[q] * dot;
+    for (int j = 0; j < k; ++j) add_to(id[j], expf(l[id[j]] - m) / z * g[j]);
   } else if (renorm) {
     float S = 0.0f, dot = 0.0f;
     for (int j = 0; j < k; ++j) {
-      const float s = 1.0f / (1.0f + expf(-l[id[j]]));
-      S += s;
-      dot += g[j] * s;
+      const float sj = 1.0f / (1.0f + expf(-l[id[j]]));
+      S += sj;
+      dot += g[j] * sj;
     }
     const float D = S + 1e-9f;
     for (int j = 0; j < k; ++j) {
-      const float s = 1.0f / (1.0f + expf(-l[id[j]]));
-      o[id[j]] += (g[j] / D - dot / (D * D)) * s * (1.0f - s);
+      const float sj = 1.0f / (1.0f + expf(-l[id[j]]));
+      add_to(id[j], (g[j] / D - dot / (D * D)) * sj * (1.0f - sj));
     }
   } else {
     for (int j = 0; j < k; ++j) {
-      const float s = 1.0f / (1.0f + expf(-l[id[j]]));
-      o[id[j]] += g[j] * s * (1.0f - s);
+      const float sj = 1.0f / (1.0f + expf(-l[id[j]]));
+      add_to(id[j], g[j] * sj * (1.0f - sj));
     }
   }
-  if (z_coef != 0.0f)
-    for (int e = 0; e < E; ++e) o[e] += z_coef * 2.0f * lse * expf(l[e] - m) / z / (float)T;
+  if (z_coef != 0.0f) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) o[q] += z_coef * 2.0f * lse * p[q] / (float)T;
+  }
   if (aux_coef != 0.0f) {
     const float scale = aux_coef * (float)E / (float)T;
-    float fp = 0.0f;
-    if (score == 0)
-      for (int e = 0; e < E; ++e) fp += (float)counts[e] / (float)T * expf(l[e] - m) / z;
-    for (int e = 0; e < E; ++e) {
+    float fl = 0.0f;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int e = lane + 64 * q;
+      if (score == 0 && e < E) fl += (float)counts[e] / (float)T * p[q];
+    }
+    const float fp = score == 0 ? wave_sum(fl) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int e = lane + 64 * q;
+      if (e >= E) continue;
       const float f = (float)counts[e] / (float)T;
       if (score == 1) {
-        const float s = 1.0f / (1.0f + expf(-l[e]));
-        o[e] += scale * f * s * (1.0f - s);
+        const float sv = 1.0f / (1.0f + expf(-v[q]));
+        o[q] += scale * f * sv * (1.0f - sv);
       } else {
-        o[e] += scale * expf(l[e] - m) / z * (f - fp);
+        o[q] += scale * p[q] * (f - fp);
       }
     }
+  }
+  float* orow = dl + t * ep;
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    const int e = lane + 64 * q;
+    if (e < ep) orow[e] = e < E ? o[q] : 0.0f;
   }
 }
 
@@ -630,8 +680,17 @@ hipError_t launch_router_bwd(int64_t T, int E, int ep, int k, const float* logit
                              const float* dtw, const int32_t* counts, int score, int renorm, float z_coef,
                              float aux_coef, float* dl, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_router_bwd, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, T, E, ep, k, logits, idx, dtw,
-                     counts, score, renorm, z_coef, aux_coef, dl);
+  if (E < 1 || ep < E || ep > 1024) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((T + 3) / 4));
+#define ROUTER_BWD(QN_)                                                                                            \
+  hipLaunchKernelGGL(k_router_bwd<QN_>, grid, dim3(256), 0, s, T, E, ep, k, logits, idx, dtw, counts, score, renorm, \
+                     z_coef, aux_coef, dl)
+  if (ep <= 64) ROUTER_BWD(1);
+  else if (ep <= 128) ROUTER_BWD(2);
+  else if (ep <= 256) ROUTER_BWD(4);
+  else if (ep <= 512) ROUTER_BWD(8);
+  else ROUTER_BWD(16);
+#undef ROUTER_BWD
   return hipGetLastError();
 }
 
