@@ -130,9 +130,11 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(int64_t T, int k, int f, con
 
 // dx_t = sum_j dXp[row_of[t, j]] (slots in order) (+ dXp[T*k + t], the
 // shared expert) (+ dxr_t, the router term).
+template <bool ROUTER>
 __global__ __launch_bounds__(256) void k_gather_bwd(int64_t T, int d, int k, const float* __restrict__ dxp,
                                                     const int32_t* __restrict__ row_of, int shared,
-                                                    const float* __restrict__ dxr, float* __restrict__ dx) {
+                                                    const float* __restrict__ dxr, const float* __restrict__ dl, int ep,
+                                                    int E, const float* __restrict__ wr, float* __restrict__ dx) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of dx
   const int nq = d / 4;
   if (i >= T * nq) return;
@@ -142,6 +144,17 @@ __global__ __launch_bounds__(256) void k_gather_bwd(int64_t T, int d, int k, con
   for (int j = 0; j < k; ++j) acc += *reinterpret_cast<const f32x4*>(dxp + (int64_t)row_of[t * k + j] * d + c);
   if (shared) acc += *reinterpret_cast<const f32x4*>(dxp + (T * k + t) * d + c);
   if (dxr) acc += *reinterpret_cast<const f32x4*>(dxr + t * d + c);
+  if constexpr (ROUTER) {
+    f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float* dlr = dl + t * ep;
+    for (int e = 0; e < E; ++e) {
+      const float a = dlr[e];
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + (size_t)e * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = __builtin_fmaf(a, w4[q], r[q]);
+    }
+    acc += r;
+  }
   *reinterpret_cast<f32x4*>(dx + t * d + c) = acc;
 }
 
@@ -593,10 +606,16 @@ hipError_t launch_swiglu_bwd(int dtype, int64_t T, int k, int f, const float* dh
 }
 
 hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const int32_t* row_of, bool shared,
-                             const float* dxr, float* dx, hipStream_t s) {
+                             const float* dxr, const float* dl, int ep, int E, const float* w_router, float* dx,
+                             hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather_bwd, dim3((unsigned)((T * (d / 4) + 255) / 256)), dim3(256), 0, s, T, d, k, dxp, row_of,
-                     (int)shared, dxr, dx);
+  const dim3 grid((unsigned)((T * (d / 4) + 255) / 256));
+  if (dl)
+    hipLaunchKernelGGL(k_gather_bwd<true>, grid, dim3(256), 0, s, T, d, k, dxp, row_of, (int)shared, dxr, dl, ep, E,
+                       w_router, dx);
+  else
+    hipLaunchKernelGGL(k_gather_bwd<false>, grid, dim3(256), 0, s, T, d, k, dxp, row_of, (int)shared, dxr, dl, ep,
+                       E, w_router, dx);
   return hipGetLastError();
 }
 

@@ -138,8 +138,12 @@ hipError_t launch_to_bf16(int64_t n, const float* in, uint16_t* out, hipStream_t
 hipError_t launch_swiglu_bwd(int dtype, int64_t T, int k, int f, const float* dhu, const float* g, const float* u,
                              const void* h, const float* w, const int32_t* row_of, bool shared, void* dgu, float* dtw,
                              float* wrow, hipStream_t s);
+// dx[t] = sum_j dxp[row_of[t, j]] (+ dxp[T*k + t], shared) (+ dxr[t]), and,
+// when dl is given, + sum_{e<E} dl[t, e] w_router[e] (the router term
+// computed in place, fp32, experts ascending; for few experts).
 hipError_t launch_gather_bwd(int64_t T, int d, int k, const float* dxp, const int32_t* row_of, bool shared,
-                             const float* dxr, float* dx, hipStream_t s);
+                             const float* dxr, const float* dl, int ep, int E, const float* w_router, float* dx,
+                             hipStream_t s);
 // Panelled operand of a K-grouped GEMM: rows in panels of P rows (one GEMM
 // tile), each panel K-blocked with K capacity kcap, so that a tile walks one
 // contiguous stretch of memory. Element (r, col), in elements, with kb = 128

@@ -49,6 +49,10 @@ moe_status check_layer(const moe_layer* L, bool need_experts) {
 // one down launch over every expert do not. A large shared expert keeps two
 // dense launches, whose tiles (and weight traffic) spread over all XCDs; as
 // the last group of the tile list its tiles would fall to one XCD.
+// The backward adds the router's input gradient dl W_router inside the final
+// gather (E fmas per element) up to this many experts, else by a GEMM.
+constexpr int kRouterInGatherMaxE = 16;
+
 bool shared_as_group(const moe_layer* L, int64_t T) {
   return L->d_ff_shared > 0 && L->d_ff_shared == L->d_ff && T * (int64_t)L->d_ff_shared <= (int64_t)1 << 25;
 }
@@ -536,7 +540,11 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   const int rbm = gemm_kg_bm(0, lo.ep, d, 1), rbn = gemm_kg_bn(rbm, d);
   MOE_TRY(launch_transpose(0, 0, dl, dlt, 1, T, lo.tp, lo.ep, 0, 0, s, rbm));    // [T, ep] -> [ep, tp]
   MOE_TRY(launch_transpose(dt, 0, x, xtr, 1, T, lo.tp, d, 0, 0, s, rbn));        // [T, d] -> [d, tp] fp32
-  MOE_TRY(launch_transpose(0, 0, L->w_router, wrt, 1, E, lo.ep, d, lo.ep, 0, s)); // [E, d] -> [d, ep]
+  // dx_router = dl W_router: a GEMM for many experts; with few, the gather
+  // below adds it in place
+  const bool router_in_gather = E <= kRouterInGatherMaxE;
+  if (!router_in_gather)
+    MOE_TRY(launch_transpose(0, 0, L->w_router, wrt, 1, E, lo.ep, d, lo.ep, 0, s)); // [E, d] -> [d, ep]
   int32_t* rkoffs = at<int32_t>(ws, lo.rkoffs);
   // nseg K segments of rseg tokens each
   int4* vg = at<int4>(ws, lo.vg);
@@ -566,19 +574,26 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   if (lo.nseg > 1)
     MOE_TRY(launch_sum_segments(at<float>(ws, lo.rpart), lo.nseg, (int64_t)lo.ep * d, (int64_t)E * d, gr->dw_router,
                                 s));
-  GemmLaunch rx{};
-  rx.dtype = 0;
-  rx.gateup = false;
-  rx.a = dl;
-  rx.b0 = wrt;
-  rx.out = at<void>(ws, lo.dxr);
-  rx.N = d;
-  rx.K = lo.ep;
-  rx.rows = T;
-  MOE_TRY(launch_gemm(rx, 128, s));
+  if (!router_in_gather) {
+    GemmLaunch rx{};
+    rx.dtype = 0;
+    rx.gateup = false;
+    rx.a = dl;
+    rx.b0 = wrt;
+    rx.out = at<void>(ws, lo.dxr);
+    rx.N = d;
+    rx.K = lo.ep;
+    rx.rows = T;
+    MOE_TRY(launch_gemm(rx, 128, s));
+  }
 
   // 8. gather^T: dx
-  MOE_TRY(launch_gather_bwd(T, d, k, at<float>(ws, lo.dxp), row_of, shared, at<float>(ws, lo.dxr), gr->dx, s));
+  if (router_in_gather)
+    MOE_TRY(launch_gather_bwd(T, d, k, at<float>(ws, lo.dxp), row_of, shared, nullptr, dl, lo.ep, E, L->w_router,
+                              gr->dx, s));
+  else
+    MOE_TRY(launch_gather_bwd(T, d, k, at<float>(ws, lo.dxp), row_of, shared, at<float>(ws, lo.dxr), nullptr, 0, 0,
+                              nullptr, gr->dx, s));
 
   // 9. weight gradients: per-group K segments of transposed activations
   int32_t* koffs = at<int32_t>(ws, lo.koffs);
