@@ -141,8 +141,10 @@ __global__ __launch_bounds__(256) void k_gather_bwd(int64_t T, int d, int k, con
   const int64_t t = i / nq;
   const int c = (int)(i % nq) * 4;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < k; ++j) acc += *reinterpret_cast<const f32x4*>(dxp + (int64_t)row_of[t * k + j] * d + c);
-  if (shared) acc += *reinterpret_cast<const f32x4*>(dxp + (T * k + t) * d + c);
+  // rows read once: streaming loads
+  for (int j = 0; j < k; ++j)
+    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dxp + (int64_t)row_of[t * k + j] * d + c));
+  if (shared) acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dxp + (T * k + t) * d + c));
   if (dxr) acc += *reinterpret_cast<const f32x4*>(dxr + t * d + c);
   if constexpr (ROUTER) {
     f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const 
       for (int q = 0; q < KG; ++q) {
         const int r = j0 + q < k ? rows_s[wave][j0 + q] : -1;
         const int rr = (r >= 0 && r < n_rows) ? r : 0;
-        v[q] = Y[(size_t)rr * n4 + c];
+        v[q] = __builtin_nontemporal_load(&Y[(size_t)rr * n4 + c]);  // read once: streaming
       }
 #pragma unroll
       for (int q = 0; q < KG; ++q) {

@@ -47,9 +47,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4):
 // lane i writes lds_wave + 16 i, where lds_wave is the same for the wave.
+// STREAM marks the load non-temporal (data read once: weights that no other
+// tile of the launch reads again).
+template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma16(const unsigned char* src, unsigned char* lds_run) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)lds_run, 16, 0, STREAM ? 2 : 0);
 }
 
 }  // namespace moe

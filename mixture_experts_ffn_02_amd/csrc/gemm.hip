@@ -258,7 +258,10 @@ void k_gemm(GemmLaunch g) {
         const int rb0 = (i - C::A_LOADS) * 4 * C::RPR;
         const unsigned char* src = (GATEUP && rb0 >= BN) ? bbase1 + (size_t)(rb0 - BN) * kbytes
                                                          : bbase0 + (size_t)rb0 * kbytes;
-        lds_dma16(src + lane_off + off_b, sb + i * 4 * C::RPR * SB);
+        if (g.b_stream)
+          lds_dma16<true>(src + lane_off + off_b, sb + i * 4 * C::RPR * SB);
+        else
+          lds_dma16(src + lane_off + off_b, sb + i * 4 * C::RPR * SB);
       }
     };
 

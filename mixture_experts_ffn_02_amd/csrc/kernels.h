@@ -67,6 +67,7 @@ constexpr int kGroupM = 8;  // default row tiles per raster group
 struct GemmLaunch {
   int dtype;               // 0 fp32, 1 bf16 (operands; accumulation fp32)
   bool gateup;             // true: out = silu(A B0^T) * (A B1^T) in dtype; false: out = A B0^T in fp32
+  bool b_stream = false;   // weight rows read once (few rows per group): non-temporal DMA
   const void* a;           // rows of K elements
   const int32_t* a_rows;   // null, or the source row of a for every grouped row (gather)
   int64_t a_row_count;     // rows of a (gather indices are clamped into range)

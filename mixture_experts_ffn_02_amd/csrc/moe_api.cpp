@@ -49,6 +49,16 @@ moe_status check_layer(const moe_layer* L, bool need_experts) {
 // one down launch over every expert do not. A large shared expert keeps two
 // dense launches, whose tiles (and weight traffic) spread over all XCDs; as
 // the last group of the tile list its tiles would fall to one XCD.
+#ifndef MOE_STREAM_TILES
+#define MOE_STREAM_TILES 1
+#endif
+// Weight rows are streamed (non-temporal DMA) when the groups average at
+// most this many row tiles: each weight tile is then read about once, and
+// keeping it in L2 only evicts data that is read again.
+bool stream_weights(int64_t rows, int64_t groups, int bm) {
+  return groups > 0 && rows <= groups * (int64_t)bm * MOE_STREAM_TILES;
+}
+
 // The backward adds the router's input gradient dl W_router inside the final
 // gather (E fmas per element) up to this many experts, else by a GEMM.
 constexpr int kRouterInGatherMaxE = 16;
@@ -221,6 +231,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   gu.tiles = tiles;
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
+  gu.b_stream = stream_weights(lo.gemm_rows, n_groups, bm);
   MOE_TRY(launch_gemm(gu, bm, s));
   mark(tm, MOE_PHASE_DOWN, s);
   GemmLaunch dn = gu;
@@ -251,6 +262,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sg.N = L->d_ff_shared;
     sg.K = d;
     sg.rows = T;
+    sg.b_stream = stream_weights(T, 1, bm_s);
     MOE_TRY(launch_gemm(sg, bm_s, s));
   }
   mark(tm, MOE_PHASE_SHARED_DOWN, s);
@@ -264,6 +276,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sd.N = d;
     sd.K = L->d_ff_shared;
     sd.rows = T;
+    sd.b_stream = stream_weights(T, 1, bm_s);
     MOE_TRY(launch_gemm(sd, bm_s, s));
     shared_out = at<float>(ws, lo.ys);
   }
@@ -473,6 +486,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   gu.tiles = tiles;
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
+  gu.b_stream = stream_weights(lo.gemm_rows, G, bm);
   MOE_TRY(launch_gemm(gu, bm, s));
 
   // 3. dy in the operand type
@@ -511,6 +525,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
   g1.tiles = tiles;
   g1.n_tiles = n_tiles;
   g1.max_m_tiles = lo.max_tiles;
+  g1.b_stream = stream_weights(lo.gemm_rows, G, bm);
   MOE_TRY(launch_gemm(g1, bm, s));
   float* wrow = at<float>(ws, lo.wrow);
   MOE_TRY(launch_swiglu_bwd(dt, T, k, f, at<float>(ws, lo.dh), at<float>(ws, lo.g), at<float>(ws, lo.u),
@@ -798,6 +813,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = max_tiles;
   gu.n_groups = n_groups;
+  gu.b_stream = stream_weights(rows, n_groups, bm);
   MOE_TRY(launch_gemm(gu, bm, s));
   GemmLaunch dn = gu;
   dn.gateup = false;
