@@ -41,9 +41,23 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
   return bf16_to_f32(v);
 }
 
-// Four consecutive elements as fp32, and back.
+// Four consecutive elements as fp32, and back. load4s: the same as a
+// streaming (non-temporal) load, for data this kernel is the last to read.
 template <typename T>
 __device__ __forceinline__ f32x4 load4(const T* p);
+template <typename T>
+__device__ __forceinline__ f32x4 load4s(const T* p);
+template <>
+__device__ __forceinline__ f32x4 load4s<float>(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+template <>
+__device__ __forceinline__ f32x4 load4s<uint16_t>(const uint16_t* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return f32x4{bf16_to_f32((uint16_t)(v.x & 0xFFFF)), bf16_to_f32((uint16_t)(v.x >> 16)),
+               bf16_to_f32((uint16_t)(v.y & 0xFFFF)), bf16_to_f32((uint16_t)(v.y >> 16))};
+}
 template <>
 __device__ __forceinline__ f32x4 load4<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
@@ -100,9 +114,9 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(int64_t T, int k, int f, con
     float dot = 0.0f;
     for (int c = tid * 4; c < f; c += 1024) {
       const int64_t i = r * f + c;
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(dhu + i);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gp + i);
-      const f32x4 uv = *reinterpret_cast<const f32x4*>(up + i);
+      const f32x4 dv = load4s<float>(dhu + i);  // read once
+      const f32x4 gv = load4s<float>(gp + i);
+      const f32x4 uv = load4s<float>(up + i);
       const f32x4 hv = load4<DT>(hp + i);
       f32x4 dg, du;
 #pragma unroll
