@@ -605,23 +605,23 @@ __global__ __launch_bounds__(256) void k_bias_update(const int32_t* __restrict__
 // rows are widened once per stage into an fp32 copy (rows padded by 16 bytes)
 // rather than by every chain that reads them.
 constexpr int kLogKC = 64;  // d is a multiple of this
-template <int TT_, int TE_, int MT_, int ME_, int NS_, int KC_ = kLogKC>
+template <int TT_, int TE_, int MT_, int ME_, int NS_, int KC_ = kLogKC, int NT_ = 256>
 struct LogitShape {
-  static constexpr int TT = TT_, TE = TE_, MT = MT_, ME = ME_, NS = NS_, KC = KC_;
+  static constexpr int TT = TT_, TE = TE_, MT = MT_, ME = ME_, NS = NS_, KC = KC_, NT = NT_;
   static constexpr int TGN = TT / MT, EGN = TE / ME;
-  static_assert(TGN * EGN == 256, "256 threads");
+  static_assert(TGN * EGN == NT && NT % 64 == 0 && NT <= 256, "threads of the block");
   static_assert(NS >= 2 && NS <= 8, "ring depth");
   static_assert(EGN <= 64 && 64 % EGN == 0, "a wave spans whole token groups");
-  static_assert(TE * KC / 4 >= 256, "the first DMA of every thread is a weight chunk");
+  static_assert(TE * KC / 4 >= NT, "the first DMA of every thread is a weight chunk");
   static constexpr int XP = KC + 4;  // fp32 token-row pitch (floats)
   template <typename XT>
   static constexpr int wch() { return TE * KC / 4; }
   template <typename XT>
   static constexpr int xch() { return TT * KC * (int)sizeof(XT) / 16; }
   template <typename XT>
-  static constexpr int loads() { return (wch<XT>() + xch<XT>() + 255) / 256; }  // DMAs per thread per stage
+  static constexpr int loads() { return (wch<XT>() + xch<XT>() + NT - 1) / NT; }  // DMAs per thread per stage
   template <typename XT>
-  static constexpr int stage_bytes() { return loads<XT>() * 4096; }
+  static constexpr int stage_bytes() { return loads<XT>() * NT * 16; }
   template <typename XT>
   static constexpr int widened_bytes() { return sizeof(XT) == 2 ? TT * XP * 4 : 0; }
   template <typename XT>
@@ -632,6 +632,8 @@ struct LogitShape {
 // 128)
 using LogitNarrow = LogitShape<16, 16, 1, 1, 5, 128>;
 using LogitNarrow64 = LogitShape<16, 16, 1, 1, 8>;
+// a handful of tokens: one wave per block, 4 tokens x 16 experts
+using LogitTiny = LogitShape<4, 16, 1, 1, 5, 128, 64>;
 // more: 2 x 4 chains, 32 x 64 blocks; many: 4 x 4 chains, 64 x 64 blocks
 // (two blocks per CU fit in LDS with bf16 tokens)
 using LogitMid = LogitShape<32, 64, 2, 4, 3>;
@@ -640,7 +642,8 @@ using LogitWide = LogitShape<64, 64, 4, 4, 2>;
 using LogitFewE = LogitShape<64, 16, 4, 1, 3>;
 
 template <typename LS, typename XT>
-__global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
+__global__ __launch_bounds__(LS::NT) void k_logits(RouteLaunch p) {
+  constexpr int NT = LS::NT;
   constexpr int TT = LS::TT, TE = LS::TE, MT = LS::MT, ME = LS::ME, NS = LS::NS, EGN = LS::EGN;
   constexpr int KC = LS::KC, CPR = KC / 4;  // 16-byte weight chunks per row and stage
   constexpr int XB = (int)sizeof(XT);
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
   const unsigned char* src[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    const int q = i * 256 + tid;
+    const int q = i * NT + tid;
     if (q < WCH) {
       const int e = q / CPR, c = (q % CPR) ^ ((e / ME) & 15);
       const int er = e0 + e < E ? e0 + e : E - 1;
@@ -682,9 +685,9 @@ __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
     const size_t wk = (size_t)st * KC * 4, xk = (size_t)st * KC * XB;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int q = i * 256 + tid;
+      const int q = i * NT + tid;
       const size_t off = (q < WCH || q >= WCH + XCH) ? wk : xk;
-      lds_dma16(src[i] + off, base + i * 4096);
+      lds_dma16(src[i] + off, base + i * NT * 16);
     }
   };
 
@@ -722,7 +725,7 @@ __global__ __launch_bounds__(256) void k_logits(RouteLaunch p) {
     if constexpr (XB == 2) {
       // widen: 8 features (16 bytes) per item; the previous stage's reads of
       // xw finished before the barrier above
-      for (int q = tid; q < TT * KC / 8; q += 256) {
+      for (int q = tid; q < TT * KC / 8; q += NT) {
         const int tt = q / (KC / 8), c = q % (KC / 8);
         const u32x4 v = *reinterpret_cast<const u32x4*>(sb + WCH * 16 + tt * KC * 2 + c * 16);
         float* o = xw + tt * XP + c * 8;
@@ -803,10 +806,10 @@ __global__ __launch_bounds__(256) void k_hist_rank(const int32_t* __restrict__ i
 }
 
 template <typename K>
-hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLaunch& a) {
+hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLaunch& a, int threads = 256) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -814,15 +817,19 @@ hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLau
 // otherwise one chain per thread while 32 x 64 blocks would not give every CU
 // one, 32 x 64 blocks while 64 x 64 ones would not give every CU two, else
 // 64 x 64.
+#ifndef LOGITS_TINY_MAX
+#define LOGITS_TINY_MAX 64
+#endif
 template <typename LS, typename XT>
 hipError_t launch_logits_shape(const RouteLaunch& a, hipStream_t s) {
   const dim3 g((unsigned)((a.T + LS::TT - 1) / LS::TT), (unsigned)((a.E + LS::TE - 1) / LS::TE));
-  return launch_k(k_logits<LS, XT>, g, 0, s, a);
+  return launch_k(k_logits<LS, XT>, g, 0, s, a, LS::NT);
 }
 template <typename XT>
 hipError_t launch_logits_t(const RouteLaunch& a, hipStream_t s) {
   const int64_t cu = cu_count(), et = (a.E + 63) / 64;
   if (a.E <= 16) return launch_logits_shape<LogitFewE, XT>(a, s);
+  if (a.T <= LOGITS_TINY_MAX && a.d % 128 == 0) return launch_logits_shape<LogitTiny, XT>(a, s);
   if ((a.T + 31) / 32 * et < cu)
     return a.d % 128 == 0 ? launch_logits_shape<LogitNarrow, XT>(a, s) : launch_logits_shape<LogitNarrow64, XT>(a, s);
   if ((a.T + 63) / 64 * et < 2 * cu) return launch_logits_shape<LogitMid, XT>(a, s);
