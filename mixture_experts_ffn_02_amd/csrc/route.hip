@@ -632,8 +632,11 @@ struct LogitShape {
 // 128)
 using LogitNarrow = LogitShape<16, 16, 1, 1, 5, 128>;
 using LogitNarrow64 = LogitShape<16, 16, 1, 1, 8>;
-// a handful of tokens: one wave per block, 4 tokens x 16 experts
-using LogitTiny = LogitShape<4, 16, 1, 1, 5, 128, 64>;
+// a handful of tokens: one wave per block, 4 tokens x 16 experts, stages of
+// 256 features four deep (128 five deep where d is not a multiple of 256):
+// long stages spread the per-stage waits and barriers over more fmas
+using LogitTiny = LogitShape<4, 16, 1, 1, 4, 256, 64>;
+using LogitTiny128 = LogitShape<4, 16, 1, 1, 5, 128, 64>;
 // more: 2 x 4 chains, 32 x 64 blocks; many: 4 x 4 chains, 64 x 64 blocks
 // (two blocks per CU fit in LDS with bf16 tokens)
 using LogitMid = LogitShape<32, 64, 2, 4, 3>;
@@ -814,12 +817,9 @@ hipError_t launch_k(K kern, dim3 grid, size_t lds, hipStream_t s, const RouteLau
 }
 
 // Logits kernel shape for a batch: at most 16 experts, 64 x 16 blocks;
-// otherwise one chain per thread while 32 x 64 blocks would not give every CU
-// one, 32 x 64 blocks while 64 x 64 ones would not give every CU two, else
-// 64 x 64.
-#ifndef LOGITS_TINY_MAX
-#define LOGITS_TINY_MAX 64
-#endif
+// otherwise one chain per thread (one-wave 4 x 16 blocks up to 64 tokens,
+// then 16 x 16 blocks while 32 x 64 blocks would not give every CU one), 32 x
+// 64 blocks while 64 x 64 ones would not give every CU two, else 64 x 64.
 template <typename LS, typename XT>
 hipError_t launch_logits_shape(const RouteLaunch& a, hipStream_t s) {
   const dim3 g((unsigned)((a.T + LS::TT - 1) / LS::TT), (unsigned)((a.E + LS::TE - 1) / LS::TE));
@@ -829,7 +829,8 @@ template <typename XT>
 hipError_t launch_logits_t(const RouteLaunch& a, hipStream_t s) {
   const int64_t cu = cu_count(), et = (a.E + 63) / 64;
   if (a.E <= 16) return launch_logits_shape<LogitFewE, XT>(a, s);
-  if (a.T <= LOGITS_TINY_MAX && a.d % 128 == 0) return launch_logits_shape<LogitTiny, XT>(a, s);
+  if (a.T <= 64 && a.d % 128 == 0)
+    return a.d % 256 == 0 ? launch_logits_shape<LogitTiny, XT>(a, s) : launch_logits_shape<LogitTiny128, XT>(a, s);
   if ((a.T + 31) / 32 * et < cu)
     return a.d % 128 == 0 ? launch_logits_shape<LogitNarrow, XT>(a, s) : launch_logits_shape<LogitNarrow64, XT>(a, s);
   if ((a.T + 63) / 64 * et < 2 * cu) return launch_logits_shape<LogitMid, XT>(a, s);

@@ -46,11 +46,14 @@ CASES = [
     C("fused_router_e128", T=32800, d_model=64, n_experts=128, top_k=8, d_ff=64, zipf_s=1.1),
     C("fused_router_e512", T=16400, d_model=64, n_experts=512, top_k=8, d_ff=64),
     C("fused_router_e1024", T=8200, d_model=64, n_experts=1024, top_k=4, d_ff=64, bias_range=0.01),
-    # split path, logits kernel with one chain per thread: ragged tokens and
-    # experts, eleven 128-feature stages (the 5-deep ring wraps), then nine
-    # 64-feature stages (d not a multiple of 128; the 8-deep ring wraps)
+    # split path, logits kernel with one chain per thread: one-wave blocks
+    # with six 256-feature stages (the 4-deep ring wraps) and eleven
+    # 128-feature stages (5-deep), ragged tokens and experts; 256-thread
+    # blocks with nine 64-feature stages (d not a multiple of 128, 8-deep)
+    C("split_tiny_ring", T=50, d_model=1536, n_experts=96, top_k=4, d_ff=64),
     C("split_narrow_ring", T=37, d_model=1408, n_experts=80, top_k=6, d_ff=64, score="sigmoid", bias_range=0.2),
     C("split_narrow_ring64", T=21, d_model=576, n_experts=64, top_k=4, d_ff=64),
+    C("split_narrow_ring128", T=300, d_model=1280, n_experts=64, top_k=4, d_ff=64),
     # split path, logits kernel with 2 x 4 chains per thread (bf16), then with
     # 4 x 4 (fp32 tokens)
     C("split_mid_ring", T=4100, d_model=256, n_experts=256, top_k=8, d_ff=64),
