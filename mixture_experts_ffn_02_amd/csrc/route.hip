@@ -89,21 +89,26 @@ ROUTE_SHAPE(512, 16, 4, 16)
 ROUTE_SHAPE(1024, 16, 4, 8)
 #undef ROUTE_SHAPE
 
-template <int EP>
+// Tokens per block of the selection that reads stored logits (split path):
+// there is no gate product to share, so small blocks spread over the chip.
+constexpr int kSelTT = 16;
+
+template <int EP, bool FROM_LOGITS = false>
 struct RouteLds {
   using S = RouteShape<EP>;
+  static constexpr int TT = FROM_LOGITS ? kSelTT : S::TT;
   // One token per thread (MT = 1): stage rows are token- and expert-major,
   // padded by 4 floats, so that a lane reads 4 features with one 16-byte
   // load. Otherwise feature-major ([feature][token] and [feature][expert]).
   static constexpr bool kRows = S::MT == 1;
   static constexpr int kPitch = kRows ? S::KC + 4 : S::KC;
-  static constexpr int kStage = 2 * kPitch * (S::TT + EP);  // floats
-  static constexpr int kLogits = S::TT * (EP + 1);          // floats
+  static constexpr int kStage = FROM_LOGITS ? 0 : 2 * kPitch * (S::TT + EP);  // floats
+  static constexpr int kLogits = TT * (EP + 1);                               // floats
   static constexpr int kUnion = kStage > kLogits ? kStage : kLogits;
-  static constexpr int kWords = (S::TT + 63) / 64;
+  static constexpr int kWords = (TT + 63) / 64;
   static size_t bytes(int k) {
-    return sizeof(float) * kUnion + sizeof(uint64_t) * EP * kWords + sizeof(int) * S::TT * k +
-           sizeof(float) * (EP + 2 * S::TT);
+    return sizeof(float) * kUnion + sizeof(uint64_t) * EP * kWords + sizeof(int) * TT * k +
+           sizeof(float) * (EP + 2 * TT);
   }
 };
 
@@ -161,8 +166,8 @@ __device__ void block_hist_rank(const int* sel, int tt_count, int k, int E, int 
 template <int EP, typename XT, bool FROM_LOGITS>
 __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   using S = RouteShape<EP>;
-  using L = RouteLds<EP>;
-  constexpr int ME = S::ME, MT = S::MT, KC = S::KC, EG = S::EG, TG = S::TG, TT = S::TT;
+  using L = RouteLds<EP, FROM_LOGITS>;
+  constexpr int ME = S::ME, MT = S::MT, KC = S::KC, EG = S::EG, TG = S::TG, TT = L::TT;
   // features per register group of the gate-product loop (fewer when a
   // thread holds many chains, to bound the registers)
   constexpr int U = (ME * MT <= 4) ? 8 : ((ME * MT <= 16) ? 4 : 2);
@@ -837,24 +842,33 @@ hipError_t launch_logits_t(const RouteLaunch& a, hipStream_t s) {
   return launch_logits_shape<LogitWide, XT>(a, s);
 }
 
+// Split path when the experts are many and whole-row blocks would not give
+// every CU two (four for shapes with at most 16 chains per thread, whose
+// fused gate product measured slower than the logits kernel's: 128 experts
+// at 512 blocks): logits first (grid over tokens and experts), then the
+// selection from them in blocks of kSelTT tokens.
+template <int EP>
+bool route_split_ep(int E, int64_t T) {
+  using S = RouteShape<EP>;
+  const int64_t nb = (T + S::TT - 1) / S::TT;
+  const int64_t per_cu = S::ME * S::MT >= 32 ? 2 : 4;
+  return E >= 64 && nb < per_cu * (int64_t)cu_count();
+}
+
 template <int EP>
 hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   using S = RouteShape<EP>;
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
+  const size_t lds_sel = RouteLds<EP, true>::bytes(a.k);
+  const int64_t nb_sel = (a.T + kSelTT - 1) / kSelTT;
   if (a.d % 64) return hipErrorInvalidValue;  // stages of 64 features (or a multiple)
-  // Split path when the experts are many and whole-row blocks would not give
-  // every CU two (four for shapes with at most 16 chains per thread, whose
-  // fused gate product measured slower than the logits kernel's: 128 experts
-  // at 512 blocks), logits first (grid over tokens and experts), then the
-  // selection.
-  const int64_t per_cu = S::ME * S::MT >= 32 ? 2 : 4;
-  const bool split = a.logits != nullptr && a.E >= 64 && nb < per_cu * (int64_t)cu_count();
+  const bool split = a.logits != nullptr && route_split_ep<EP>(a.E, a.T);
   if (split) {
     hipError_t e = a.dtype == 1 ? launch_logits_t<uint16_t>(a, s) : launch_logits_t<float>(a, s);
     if (e != hipSuccess) return e;
-    return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, true>, dim3((unsigned)nb), lds, s, a)
-                        : launch_k(k_route<EP, float, true>, dim3((unsigned)nb), lds, s, a);
+    return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, true>, dim3((unsigned)nb_sel), lds_sel, s, a)
+                        : launch_k(k_route<EP, float, true>, dim3((unsigned)nb_sel), lds_sel, s, a);
   }
   return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, false>, dim3((unsigned)nb), lds, s, a)
                       : launch_k(k_route<EP, float, false>, dim3((unsigned)nb), lds, s, a);
@@ -868,16 +882,16 @@ int padded_experts(int E) {
 
 }  // namespace
 
-int route_tokens_per_block(int E) {
+int route_tokens_per_block(int E, int64_t T) {
   switch (padded_experts(E)) {
-    case 8: return RouteShape<8>::TT;
-    case 16: return RouteShape<16>::TT;
-    case 32: return RouteShape<32>::TT;
-    case 64: return RouteShape<64>::TT;
-    case 128: return RouteShape<128>::TT;
-    case 256: return RouteShape<256>::TT;
-    case 512: return RouteShape<512>::TT;
-    default: return RouteShape<1024>::TT;
+    case 8: return route_split_ep<8>(E, T) ? kSelTT : RouteShape<8>::TT;
+    case 16: return route_split_ep<16>(E, T) ? kSelTT : RouteShape<16>::TT;
+    case 32: return route_split_ep<32>(E, T) ? kSelTT : RouteShape<32>::TT;
+    case 64: return route_split_ep<64>(E, T) ? kSelTT : RouteShape<64>::TT;
+    case 128: return route_split_ep<128>(E, T) ? kSelTT : RouteShape<128>::TT;
+    case 256: return route_split_ep<256>(E, T) ? kSelTT : RouteShape<256>::TT;
+    case 512: return route_split_ep<512>(E, T) ? kSelTT : RouteShape<512>::TT;
+    default: return route_split_ep<1024>(E, T) ? kSelTT : RouteShape<1024>::TT;
   }
 }
 
