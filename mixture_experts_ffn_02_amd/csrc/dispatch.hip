@@ -91,8 +91,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
   const int b0 = g * chunk, b1 = min(nb, b0 + chunk);
   int s = 0;
   if (e < E) {
-    // the loads of a thread's blocks are independent: batch them
+    // the loads of a thread's blocks are independent: batch them (16, then 8)
     int b = b0;
+    for (; b + 16 <= b1; b += 16) {
+      int v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = hist[(size_t)(b + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s += v[q];
+    }
     for (; b + 8 <= b1; b += 8) {
       int v[8];
 #pragma unroll
@@ -130,6 +137,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict
   if (e < E) {
     int run = cnt[e] + part[tid] - s;  // rows of expert e before block b0
     int b = b0;
+    for (; b + 16 <= b1; b += 16) {
+      int v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = hist[(size_t)(b + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        base[(size_t)(b + q) * E + e] = run;
+        run += v[q];
+      }
+    }
     for (; b + 8 <= b1; b += 8) {
       int v[8];
 #pragma unroll
