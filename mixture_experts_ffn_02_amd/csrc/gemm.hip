@@ -486,19 +486,26 @@ int cu_count() {
 // such tiles and there are enough of them to give every CU several (the
 // persistent grid has one 256-row block per CU), else 128 (less padding in
 // short groups, four times as many tiles).
-int gemm_bm(int dtype, int64_t rows, int64_t groups, int n) {
+int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
   if (dtype != 1 || groups <= 0) return 128;
   const int64_t avg = rows / groups;
   // Few rows per group (small batches, many experts): the weights dominate
-  // the traffic, and 64-row tiles with wider weight tiles stage half as many
+  // the traffic, and 64-row tiles with wider weight tiles stage fewer
   // padding rows per weight byte, as long as their tiles still give every
   // block slot of the persistent grid one (else more, narrower tiles win;
-  // at most `rows` groups hold rows).
+  // at most `rows` groups hold rows). Measured up to 128 rows per group:
+  // 3-6% faster than 128-row tiles at 72-112 rows of 256 experts with
+  // d_in 7168, 3% at 96-128 rows of 128 experts with d_in 2048.
   const int64_t busy = groups < rows ? groups : rows;
   const int64_t tiles64 = busy * (n % 128 == 0 ? n / 128 : n / 64);
-  if (avg <= 64 && tiles64 >= 2 * (int64_t)cu_count()) return 64;
+  if (avg <= 128 && tiles64 >= 2 * (int64_t)cu_count()) return 64;
+  // 256-row tiles read each weight panel once per group: they pay for their
+  // padding with many rows per group, or with a long K, where a 128-row
+  // pair re-reads multi-MB panels that do not stay in L2 (d_in 7168: 3% at
+  // 144 rows per group, 1% at 288; d_in 2048 at 256 rows: 7% slower)
   const int64_t tiles256 = (rows / 256) * (n / 128);
-  return (avg >= 768 && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
+  const bool long_k = d_in >= 4096;
+  return ((avg >= 768 || long_k) && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
 }
 
 // Row tile of a K-grouped (weight-gradient) GEMM: bf16 takes 256 x 256 tiles

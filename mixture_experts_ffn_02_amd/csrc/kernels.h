@@ -125,9 +125,10 @@ __host__ __device__ inline float* kg_out_row(const GemmLaunch& g, int grp, int m
     base = static_cast<float*>(g.out) + (size_t)grp * rows0 * g.N;
   return base + (size_t)(second ? mm - g.m0 : mm) * g.N;
 }
-// Row tile (64, 128 or 256) for `rows` rows in `groups` groups and n output
-// columns; the tile list of a grouped launch must be built with the same value.
-int gemm_bm(int dtype, int64_t rows, int64_t groups, int n);
+// Row tile (64, 128 or 256) for `rows` rows in `groups` groups, n output
+// columns of the gate/up product and its K = d_in; the tile list of a grouped
+// launch must be built with the same value.
+int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in);
 // Smallest row tile of a grouped launch: tile lists hold at most
 // rows / kMinTileRows + groups entries.
 constexpr int kMinTileRows = 64;

@@ -196,7 +196,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   const bool merged = shared_as_group(L, T);
   if (merged && T * (int64_t)(k + 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
   const int n_groups = E + (merged ? 1 : 0);
-  const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff);
+  const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model);
   const int tpb = route_tokens_per_block(E, T);
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
@@ -249,7 +249,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
 
   // shared expert: rows T*k .. T*k+T-1 of the grouped output, or its own GEMMs
   const float* shared_out = merged ? at<float>(ws, lo.yperm) + (size_t)T * k * d : nullptr;
-  const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared);
+  const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared, L->d_model);
   mark(tm, MOE_PHASE_SHARED_GATEUP, s);
   if (L->d_ff_shared > 0 && !merged) {
     GemmLaunch sg{};
@@ -457,7 +457,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, int64_t T, const int3
 
   // 1. dispatch of the given routing (shared expert as group E)
   const int tpb = hist_tokens_per_block();
-  const int bm = gemm_bm(dt, lo.gemm_rows, G, f);
+  const int bm = gemm_bm(dt, lo.gemm_rows, G, f, L->d_model);
   MOE_TRY(launch_hist_rank(topk_idx, T, k, E, hist, rank, s));
   MOE_TRY(launch_scan(hist, (int)lo.nb, E, counts, offsets, base, bm, n_tiles, tiles, s, shared ? T : 0));
   MOE_TRY(launch_scatter(topk_idx, rank, base, T, k, E, tpb, row_of, tok_of_row, nullptr, nullptr, 0, s, shared));
@@ -793,7 +793,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const int bm = gemm_bm(dtype, rows, n_groups, d_ff);
+  const int bm = gemm_bm(dtype, rows, n_groups, d_ff, d_in);
   const int64_t max_tiles = (rows + kMinTileRows - 1) / kMinTileRows + n_groups;
   int32_t* n_tiles = at<int32_t>(ws, 0);
   int2* tiles = at<int2>(ws, align_up(sizeof(int32_t)));
