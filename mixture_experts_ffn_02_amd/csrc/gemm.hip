@@ -81,6 +81,22 @@ struct Cfg {
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// XOR key of K row kr of a transposed-weight stage (rows of 2*BN bytes): a
+// transposing read takes, per 16-lane group, 8 bytes from each of 4
+// consecutive rows and 4 consecutive 16-byte chunks' halves; keys 0/4/8/12
+// (rows of at least 16 chunks) or 0/0/4/4 (8-chunk rows, whose odd rows sit
+// 128 bytes further in the bank window) put two groups' 32 reads in 32
+// distinct bank pairs.
+template <int BN>
+__device__ __forceinline__ int tkey(int kr) {
+  if constexpr (BN >= 128)
+    return 4 * (kr & 3);
+  else
+    return 4 * ((kr >> 1) & 1);
+}
 
 // One 32 x 32 MFMA tile over the 16 bytes of K that each lane holds: lane l
 // provides row l % 32 of A (and column l % 32 of B) for K group l / 32.
@@ -142,11 +158,18 @@ __device__ __forceinline__ float to_out<float>(float v) {
 // BWD: the backward-pass variants: gate/up that also stores the fp32
 // pre-activations (GATEUP), the K-grouped weight gradients (otherwise); the
 // forward kernels compile without them.
-template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF, bool BWD>
+// BT (bf16, plain product): the weights are stored [K, N] per group (N
+// contiguous), as the backward products dy W_down and [dG | dU] [W_gate ;
+// W_up] find them; a stage holds KE rows of BN columns, and the fragment reads
+// transpose them with ds_read_b64_tr_b16, so the weights need no transposed
+// copy.
+template <typename DT, bool GATEUP, bool GROUPED, int BM, int BN, int SB, int NBUF, bool BWD, bool BT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Cfg<DT, GATEUP, BM, BN, SB, NBUF>::OCC)))
 void k_gemm(GemmLaunch g) {
+  static_assert(!BT || (!GATEUP && !BWD && sizeof(DT) == 2 && SB == 128 && BN >= 64), "transposed-weight variant");
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
   __shared__ __align__(16) unsigned char lds[NBUF * C::STAGE];
+  __attribute__((address_space(3))) unsigned char* const lds_as3 = (__attribute__((address_space(3))) unsigned char*)lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int n_tiles_n = g.N / BN;
@@ -227,6 +250,14 @@ void k_gemm(GemmLaunch g) {
     const unsigned char* B1 = !GATEUP ? B0
                               : xg    ? reinterpret_cast<const unsigned char*>(g.bx1)
                                       : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * g.N * kbytes;
+    // BT: this group's [K, N] weights, K rows below bt_ksplit from b0 (bx0),
+    // the rest from b1 (bx1)
+    const size_t ldb = (size_t)g.N * 2;
+    const int64_t kfirst = g.bt_ksplit > 0 ? g.bt_ksplit : g.K;
+    const unsigned char* T0 = xg ? reinterpret_cast<const unsigned char*>(g.bx0)
+                                 : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)grp * kfirst * ldb;
+    const unsigned char* T1 = xg ? reinterpret_cast<const unsigned char*>(g.bx1)
+                                 : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)grp * (g.K - kfirst) * ldb;
 
     // Source row of each A run of this lane. Rows past the tile's end read a
     // valid row; their results are never stored. Weight rows are addressed
@@ -253,6 +284,26 @@ void k_gemm(GemmLaunch g) {
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
         lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + off_a + lchunk * 16, sb + i * 4 * C::RPR * SB);
+      if constexpr (BT) {
+        // KE rows of 2*BN bytes; 1 KB run r of the region holds bytes
+        // r*1024 .. of it, lane l's 16 bytes at physical chunk pc of row kr,
+        // which takes logical chunk pc ^ tkey(kr)
+        const int k0 = kt * C::KE;
+        const bool second = g.bt_ksplit > 0 && k0 >= g.bt_ksplit;
+        const unsigned char* tb = second ? T1 + (size_t)(k0 - g.bt_ksplit) * ldb : T0 + (size_t)k0 * ldb;
+        tb += (size_t)n0 * 2;
+#pragma unroll
+        for (int i = C::A_LOADS; i < C::LPS; ++i) {
+          const int byte = ((i - C::A_LOADS) * 4 + wave) * 1024 + lane * 16;
+          const int kr = byte / (2 * BN), pc = (byte % (2 * BN)) >> 4;
+          const unsigned char* src = tb + (size_t)kr * ldb + ((pc ^ tkey<BN>(kr)) << 4);
+          if (g.b_stream)
+            lds_dma16<true>(src, sb + i * 4 * C::RPR * SB);
+          else
+            lds_dma16(src, sb + i * 4 * C::RPR * SB);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = C::A_LOADS; i < C::LPS; ++i) {
         const int rb0 = (i - C::A_LOADS) * 4 * C::RPR;
@@ -287,6 +338,27 @@ void k_gemm(GemmLaunch g) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
         f.a[i] = *reinterpret_cast<const u32x4*>(base + C::swz(wm * C::TM + i * 32 + (lane & 31), ch));
+      if constexpr (BT) {
+        // lane l: column l % 32 of the 32-column tile, K rows 16s + 8(l/32)
+        // + 0..7 as two transposing reads of 4 rows; within each 16-lane
+        // group, lane L addresses row L/4 of the 4 and columns 4(L%4) .. +3
+        const int grp16 = lane >> 4, L = lane & 15;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int n = wn * C::TN + j * 32 + 16 * (grp16 & 1) + 4 * (L & 3);
+          const int c = n >> 3, half = (n >> 2) & 1;
+          u32x2 q[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int kr = 16 * s + 8 * (grp16 >> 1) + 4 * t + (L >> 2);
+            const int off = BM * SB + kr * (2 * BN) + ((c ^ tkey<BN>(kr)) << 4) + half * 8;
+            q[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (__attribute__((address_space(3))) v4i16*)(lds_as3 + (base - lds) + off)));
+          }
+          f.b[0][j] = u32x4{q[0][0], q[0][1], q[1][0], q[1][1]};
+        }
+        return;
+      }
 #pragma unroll
       for (int h = 0; h < C::NG; ++h)
 #pragma unroll
@@ -351,7 +423,7 @@ void k_gemm(GemmLaunch g) {
         if (s + 1 < C::SPS) {
           load_frag(nxt, kt, s + 1);
           mma(cur);
-          interleave<C::NG * C::FM * C::FN, C::FM + C::NG * C::FN, 0>();
+          interleave<C::NG * C::FM * C::FN, C::FM + (BT ? 2 : 1) * C::NG * C::FN, 0>();
         } else {
           // stages in flight beyond kt+1: kt+2 .. min(kt+NBUF-1, nk-1)
           const int last = (kt + NBUF - 1 < nk - 1) ? kt + NBUF - 1 : nk - 1;
@@ -361,7 +433,7 @@ void k_gemm(GemmLaunch g) {
           if (kt + NBUF < nk) issue(kt + NBUF);
           if (kt + 1 < nk) load_frag(nxt, kt + 1, 0);
           mma(cur);
-          interleave<C::NG * C::FM * C::FN, C::FM + C::NG * C::FN, C::LPS>();
+          interleave<C::NG * C::FM * C::FN, C::FM + (BT ? 2 : 1) * C::NG * C::FN, C::LPS>();
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -446,7 +518,7 @@ void k_gemm(GemmLaunch g) {
   }
 }
 
-template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF, bool BWD = false>
+template <typename DT, bool GATEUP, int BM, int BN, int SB, int NBUF, bool BWD = false, bool BT = false>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
   using C = Cfg<DT, GATEUP, BM, BN, SB, NBUF>;
   if (g.N % BN || (!g.koffs && g.K % C::KE)) return hipErrorInvalidValue;
@@ -460,9 +532,9 @@ hipError_t launch_t(const GemmLaunch& g, hipStream_t s) {
     blocks = need < blocks ? need : blocks;
   }
   if (g.offsets)
-    hipLaunchKernelGGL((k_gemm<DT, GATEUP, true, BM, BN, SB, NBUF, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, true, BM, BN, SB, NBUF, BWD, BT>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL((k_gemm<DT, GATEUP, false, BM, BN, SB, NBUF, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm<DT, GATEUP, false, BM, BN, SB, NBUF, BWD, BT>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -553,6 +625,23 @@ hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
     return wide ? launch_t<float, false, 64, 128, 128, 2, true>(g, s) : launch_t<float, false, 64, 64, 128, 2, true>(g, s);
   }
   if (bm == 64 && (g.dtype != 1 || g.koffs)) return hipErrorInvalidValue;
+  if (g.bt) {  // weights stored [K, N]
+    if (g.dtype != 1 || g.gateup || g.out_g || g.bt_ksplit < 0 || g.bt_ksplit % 64 || g.bt_ksplit >= g.K ||
+        (g.extra_group >= 0 && !g.bx0) || (g.bt_ksplit > 0 && (!g.b1 || (g.extra_group >= 0 && !g.bx1))))
+      return hipErrorInvalidValue;
+    if (bm == 64) {
+      if (g.N % 256 == 0) return launch_t<uint16_t, false, 64, 256, 128, 2, false, true>(g, s);
+      if (g.N % 128 == 0) return launch_t<uint16_t, false, 64, 128, 128, 2, false, true>(g, s);
+      return launch_t<uint16_t, false, 64, 64, 128, 2, false, true>(g, s);
+    }
+    if (bm == 256) {
+      if (g.N % 256 == 0) return launch_t<uint16_t, false, 256, 256, 128, 2, false, true>(g, s);
+      if (g.N % 128 == 0) return launch_t<uint16_t, false, 256, 128, 128, 2, false, true>(g, s);
+      return launch_t<uint16_t, false, 256, 64, 128, 2, false, true>(g, s);
+    }
+    if (g.N % 128 == 0) return launch_t<uint16_t, false, 128, 128, 128, 2, false, true>(g, s);
+    return launch_t<uint16_t, false, 128, 64, 128, 2, false, true>(g, s);
+  }
   if (g.out_g) {  // gate/up that also stores the pre-activations (backward recompute)
     if (!g.gateup) return hipErrorInvalidValue;
     if (g.dtype == 1) {

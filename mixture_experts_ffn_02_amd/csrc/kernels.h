@@ -81,6 +81,11 @@ struct GemmLaunch {
   const void* bx1 = nullptr;  // [N, K] (gateup)
   void* out;               // [rows, N]
   int N, K;
+  // bf16 plain product only: b0 / b1 / bx0 / bx1 hold [K, N] (N contiguous)
+  // per group instead of [N, K]; K rows below bt_ksplit (a multiple of 64)
+  // come from b0 / bx0, the others from b1 / bx1 (0: all from b0 / bx0)
+  bool bt = false;
+  int bt_ksplit = 0;
   // grouped mode: tile list from launch_scan / launch_tiles_from_offsets
   const int32_t* offsets;  // [G+1] or null for one dense group of `rows` rows
   const int2* tiles;
