@@ -467,16 +467,23 @@ __global__ __launch_bounds__(1024) void k_kg_setup(int G, const int32_t* __restr
 // thread per 4 columns of one row; blockIdx.y picks the cut group.
 __global__ __launch_bounds__(256) void k_kg_reduce(GemmLaunch g, const int4* __restrict__ red,
                                                    const int32_t* __restrict__ n_red) {
-  if ((int)blockIdx.y >= n_red[0]) return;  // uniform
-  const int4 r = red[blockIdx.y];
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= (int64_t)g.m_valid * g.N) return;
-  const int mm = (int)(i / g.N), col = (int)(i % g.N);
-  float* dst = kg_out_row(g, r.x, mm) + col;
-  f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
-  for (int q = 0; q < r.z; ++q)
-    acc += *reinterpret_cast<const f32x4*>(g.part + ((size_t)(r.y + q) * g.m_rows + mm) * g.N + col);
-  *reinterpret_cast<f32x4*>(dst) = acc;
+  // blocks of row y of the grid stride over the 4-column pieces of cut
+  // groups y, y + gridDim.y, ... (the grid is sized by the pieces of one
+  // group and a few groups at a time, not by the bound on cut groups)
+  const int nr = n_red[0];
+  const int64_t n4 = (int64_t)g.m_valid * g.N / 4;
+  for (int ri = blockIdx.y; ri < nr; ri += gridDim.y) {
+    const int4 r = red[ri];
+    for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < n4; p += (int64_t)gridDim.x * 256) {
+      const int64_t i = p * 4;
+      const int mm = (int)(i / g.N), col = (int)(i % g.N);
+      float* dst = kg_out_row(g, r.x, mm) + col;
+      f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
+      for (int q = 0; q < r.z; ++q)
+        acc += *reinterpret_cast<const f32x4*>(g.part + ((size_t)(r.y + q) * g.m_rows + mm) * g.N + col);
+      *reinterpret_cast<f32x4*>(dst) = acc;
+    }
+  }
 }
 
 // Router logit gradients in fp32, one wave per token and a lane per expert
@@ -706,8 +713,10 @@ hipError_t launch_kg_setup(int G, const int32_t* offsets, int kp, int mt, int32_
 hipError_t launch_kg_reduce(const GemmLaunch& g, const int4* red, const int32_t* n_red, int max_red, hipStream_t s) {
   if (max_red <= 0 || g.m_valid <= 0 || g.N % 4) return hipSuccess;
   const int64_t n4 = (int64_t)g.m_valid * g.N / 4;
-  hipLaunchKernelGGL(k_kg_reduce, dim3((unsigned)((n4 + 255) / 256), (unsigned)max_red), dim3(256), 0, s, g, red,
-                     n_red);
+  const int gy = max_red < 16 ? max_red : 16;
+  const int64_t cap = (int64_t)cu_count() * 32 / gy;  // blocks per group row: enough to stream its pieces
+  const int64_t blocks = (n4 + 255) / 256 < cap ? (n4 + 255) / 256 : (cap > 0 ? cap : 1);
+  hipLaunchKernelGGL(k_kg_reduce, dim3((unsigned)blocks, (unsigned)gy), dim3(256), 0, s, g, red, n_red);
   return hipGetLastError();
 }
 
