@@ -471,7 +471,12 @@ void k_gemm(GemmLaunch g) {
           const u32x4 val = *reinterpret_cast<const u32x4*>(scr + r * P + c16 * 16);
           const int m = wm * C::TM + i * 32 + r;
           const int n = n0 + wn * C::TN + j * 32 + c16 * (16 / EB);
-          if (m < rows) *reinterpret_cast<u32x4*>(row_ptr(m) + (size_t)n * EB) = val;
+          if (m < rows) {
+            if constexpr (kg)  // weight gradients and partials: streaming stores (measured faster)
+              __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(row_ptr(m) + (size_t)n * EB));
+            else
+              *reinterpret_cast<u32x4*>(row_ptr(m) + (size_t)n * EB) = val;
+          }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
