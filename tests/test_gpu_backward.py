@@ -77,6 +77,10 @@ CASES = [
     C("bwd_f32_one_token", T=1, d_model=128, n_experts=8, top_k=4, d_ff=128, dtype="f32", score="sigmoid",
       shared=True),
     C("bwd_bf16_e1024", T=384, d_model=64, n_experts=1024, top_k=8, d_ff=64, bias_range=0.1),
+    # stored-weight products with 64-column tiles (d and d_ff not multiples of
+    # 128) and W_gate / W_up meeting at K row 320 of the 640
+    C("bwd_bf16_narrow_split", T=700, d_model=192, n_experts=12, top_k=3, d_ff=320, score="sigmoid", shared=True,
+      bias_range=0.2),
     # more than 2048 rows per expert: the bf16 backward products read
     # transposed weight copies instead of the stored [K, N] weights
     C("bwd_bf16_many_rows", T=4500, d_model=128, n_experts=2, top_k=1, d_ff=192, shared=True),
