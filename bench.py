@@ -1,15 +1,19 @@
 """Throughput of the MoE FFN layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload small_sigmoid]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload deepseek_fine]
 
 One step is one moe_forward call (route, dispatch, routed and shared SwiGLU
 experts, combine) over one batch of seeded synthetic tokens that are already
-resident in HBM. Prints one JSON line with the whole-job throughput, the
+resident in HBM. The default workload is the largest layer that fits one GPU
+(DeepSeek-style: 65,536 tokens, d_model 7168, 256 routed experts + 1 shared,
+top-8, d_ff 2048). Prints one JSON line with the whole-job throughput, the
 roofline of the dominant kernel (the routed gate/up grouped GEMM, timed with
 hipEvents on the layer's stream around each of its launches in the timed
 region), per-phase times from a second pass of the same steps with every
-phase boundary timed, the backward pass, and the CPU oracle timed on a
-bounded sample of the same workload.
+phase boundary timed, the same phases with cold caches (a 1 GiB copy between
+steps, outside the timed events, evicts L2 and the 256 MB last-level cache),
+the backward pass where it fits, and the CPU oracle timed on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -35,14 +39,45 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small_sigmoid")
+    ap.add_argument("--workload", default="deepseek_fine")
     ap.add_argument("--tokens", type=int, default=0, help="override the workload's token count (small-T sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--cold-steps", type=int, default=10, help="steps timed with cold caches (0: none)")
     return ap.parse_args()
+
+
+FLUSH_BYTES = 1 << 30  # copied between cold steps: 4x the last-level cache
+
+
+def host_cpu():
+    """CPU model and logical CPU count from lscpu (None when unavailable)."""
+    import subprocess
+
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None, None
+    for line in out.splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            info[k.strip()] = v.strip()
+    n = info.get("CPU(s)")
+    return info.get("Model name"), (int(n) if n and n.isdigit() else None)
+
+
+def oracle_threads() -> int:
+    """Every CPU of the affinity mask, within the CPU share the environment
+    grants (OMP_NUM_THREADS, when it is set)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -126,7 +161,7 @@ def measure_backward(cfg, layer, x, steps: int, warmup: int):
 
 
 def cpu_baseline(cfg, inputs, target_s: float):
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = oracle_threads()
     os.environ["OMP_NUM_THREADS"] = str(threads)
     import oracle
     import numpy as np
@@ -146,10 +181,35 @@ def cpu_baseline(cfg, inputs, target_s: float):
     while t < target_s and reps < 64:  # the whole layer takes less than the target: repeat it
         t += run(n)
         reps += 1
+    model, ncpu = host_cpu()
     return {"value": round(n * reps / t, 2), "unit": "tokens/s", "cores": oracle.lib().oracle_num_threads(),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same layer, {reps} run(s): fp32 router + fp64 experts "
-                      f"and combine, {t:.2f} s in all"}
+                      f"and combine, {t:.2f} s in all",
+            "cpu_model": model, "host_cpus": ncpu, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cold_phases(layer, x, y, steps: int):
+    """Per-phase times (ms) of `steps` forward calls, each after a 1 GiB
+    device copy that evicts L2 and the last-level cache; the copy runs
+    before the step's first event, so no phase includes it."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_02_amd.layer import Timing
+
+    src = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device).fill_(1.0)
+    dst = torch.empty_like(src)
+    timings = [Timing() for _ in range(steps)]
+    for t in timings:
+        dst.copy_(src)
+        layer.forward(x, y, want_routing=False, timing=t)
+    torch.cuda.synchronize()
+    ph = [t.read() for t in timings]
+    for t in timings:
+        t.close()
+    del src, dst
+    return {k: float(np.mean([p[k] for p in ph])) for k in ph[0]}
 
 
 def main():
@@ -214,22 +274,26 @@ def main():
     roofline = {"bound": "mfma", "kernel": f"k_gemm<{cfg.dtype}, gate/up, grouped> ({what})",
                 "achieved": round(gu, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
-    detail = {}
-    for name, w in work.items():
-        t_s = phase_ms[name] * 1e-3
-        if t_s <= 0 or not (w.get("flops") or w.get("bytes")):
-            continue  # a phase that launched nothing (no shared expert)
-        e = {"ms": round(phase_ms[name], 4)}
-        if "flops" in w and w["flops"]:
-            tf = w["flops"] / t_s / 1e12
-            pk = PEAK_VALU_F32_TFLOPS if name == "route" else peak
-            e.update(tflops=round(tf, 2), frac_compute_peak=round(tf / pk, 4))
-        if w.get("bytes"):
-            gbs = w["bytes"] / t_s / 1e9
-            e.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
-        detail[name] = e
-    for name in ("scan", "scatter"):
-        detail[name] = {"ms": round(phase_ms[name], 4)}
+    def phase_detail(pms):
+        detail = {}
+        for name, w in work.items():
+            t_s = pms[name] * 1e-3
+            if t_s <= 0 or not (w.get("flops") or w.get("bytes")):
+                continue  # a phase that launched nothing (no shared expert)
+            e = {"ms": round(pms[name], 4)}
+            if "flops" in w and w["flops"]:
+                tf = w["flops"] / t_s / 1e12
+                pk = PEAK_VALU_F32_TFLOPS if name == "route" else peak
+                e.update(tflops=round(tf, 2), frac_compute_peak=round(tf / pk, 4))
+            if w.get("bytes"):
+                gbs = w["bytes"] / t_s / 1e9
+                e.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+            detail[name] = e
+        for name in ("scan", "scatter"):
+            detail[name] = {"ms": round(pms[name], 4)}
+        return detail
+
+    detail = phase_detail(phase_ms)
     # expert GEMM phases that ran (the shared expert's own launches only when it has them)
     gemm_phases = [n for n in ("gateup", "down", "shared_gateup", "shared_down") if n in work and work[n]["flops"]]
 
@@ -255,6 +319,12 @@ def main():
             sum(work[n]["flops"] for n in gemm_phases) / (sum(phase_ms[n] for n in gemm_phases) * 1e-3)
             / 1e12 / peak, 4),
     }
+    if args.cold_steps > 0:
+        cold = cold_phases(layer, x, y, args.cold_steps)
+        out["phases_cold"] = phase_detail(cold)
+        out["phases_cold"]["ms_per_step"] = round(sum(cold.values()), 4)
+        out["phases_cold"]["note"] = (f"{args.cold_steps} steps, each after a {FLUSH_BYTES >> 20} MiB device copy "
+                                      "outside the timed events (L2 and the last-level cache evicted)")
     # expert weights the step had to read: experts that received tokens (+ the shared one)
     counts = layer.route(x)["counts"].cpu().numpy()
     used = int((counts > 0).sum())

@@ -39,10 +39,19 @@ def gpu_forward(layer: MoELayer, x: torch.Tensor):
 
 
 def assert_routing(g, o, what=""):
+    """Expert ids, counts and combine weights bit-exact. The weights are
+    formed on both sides by the same IEEE operation sequence (the canonical
+    exp of the router, fp32 sums over the chosen slots in slot order, one
+    correctly rounded division), so equal bits also pin the kernel's exp to
+    the oracle's."""
     assert np.array_equal(g["idx"], o["idx"]), f"{what}: expert ids differ at {np.argwhere(g['idx'] != o['idx'])[:5]}"
     assert np.array_equal(g["counts"], o["counts"]), f"{what}: counts differ"
-    rel = np.abs(g["w"].astype(np.float64) - o["w"]) / np.abs(o["w"].astype(np.float64)).clip(1e-30)
-    assert rel.max() <= 1e-6, f"{what}: weights rel err {rel.max():.3e}"
+    gw, ow = np.asarray(g["w"], np.float32), np.asarray(o["w"], np.float32)
+    if not np.array_equal(gw.view(np.uint32), ow.view(np.uint32)):
+        bad = np.argwhere(gw.view(np.uint32) != ow.view(np.uint32))
+        rel = np.abs(gw.astype(np.float64) - ow) / np.abs(ow.astype(np.float64)).clip(1e-30)
+        raise AssertionError(f"{what}: combine weights differ in {len(bad)} places, first {bad[:5].tolist()}, "
+                             f"max rel err {rel.max():.3e}")
 
 
 # bf16 keeps 8 significant bits: rounding to nearest moves a value by at most
@@ -86,18 +95,19 @@ def assert_output(cfg: LayerConfig, y_gpu: np.ndarray, y_ref: np.ndarray, what="
     return err / r
 
 
-def check_y(cfg, inp, o, y_gpu, tokens=None):
+def check_y(cfg, inp, o, y_gpu, tokens=None, rms_bar=False):
     """fp32 layers: max|err| <= 1e-5 RMS(y). bf16 layers: every element within
-    the bf16-activation envelope; the layers named in the workload table also
-    meet max|err| <= 2e-2 RMS(y). (Narrow test shapes with d_ff of 64 cannot
-    meet the RMS bound with any bf16 activation: a numpy simulation of the
-    rounding alone gives 0.02-0.04 there.)"""
+    the bf16-activation envelope; the layers named in the workload table, and
+    those marked rms_bar (wide experts), also meet max|err| <= 2e-2 RMS(y).
+    (Narrow test shapes with d_ff of 64 cannot meet the RMS bound with any
+    bf16 activation: a numpy simulation of the rounding alone gives 0.02-0.04
+    there.)"""
     y_ref = o["y"]
     if cfg.dtype == "f32":
         return assert_output(cfg, y_gpu, y_ref, cfg.name)
     worst = assert_within_envelope(y_gpu, y_ref, output_envelope(cfg, inp, o, tokens), cfg.name)
     ratio = rms_ratio(y_gpu, y_ref)
     print(f"{cfg.name}: max|err|/RMS = {ratio:.3e}, worst error/envelope = {worst:.3f}")
-    if cfg.name in CONFIGS:
+    if cfg.name in CONFIGS or rms_bar:
         assert_output(cfg, y_gpu, y_ref, cfg.name)
     return ratio

@@ -84,6 +84,11 @@ CASES = [
     # more than 2048 rows per expert: the bf16 backward products read
     # transposed weight copies instead of the stored [K, N] weights
     C("bwd_bf16_many_rows", T=4500, d_model=128, n_experts=2, top_k=1, d_ff=192, shared=True),
+    # 256-row GEMM tiles: 2048 rows per expert (the stored-weight products
+    # with 256 x 256 tiles), and 8192 rows per expert (transposed weight
+    # copies with 256-row tiles), every gradient element against the oracle
+    C("bwd_bf16_tiles256", T=8192, d_model=512, n_experts=32, top_k=8, d_ff=1024, score="sigmoid", bias_range=0.1),
+    C("bwd_bf16_tiles256_copies", T=16384, d_model=512, n_experts=8, top_k=4, d_ff=1024),
 ]
 COEF = {"bwd_f32_softmax": (1e-3, 1e-3), "bwd_bf16_sigmoid_shared": (1e-3, 1e-3)}
 
@@ -100,6 +105,7 @@ def run_case(cfg, seed=7):
     return inp, idx, w, dy, zc, ac, {n: to_host(v) for n, v in g.items()}
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 def test_backward_matches_oracle(cfg):
     print(f"[case] {cfg.name}", flush=True)

@@ -4,9 +4,11 @@ the z-loss and aux-loss coefficients at zero, a token's dx and combine-weight
 gradients depend on that token alone, and an expert's weight gradients on the
 tokens routed to it, so the oracle's backward over those tokens gives them
 exactly. Sampled: 64 random tokens, the ragged tail, the tokens of the least
-loaded expert; the weight gradients of that expert where it has at most 256
-tokens (at the iso-width layer every expert has thousands, more than the
-oracle computes in a test).
+loaded expert; and the weight gradients of that expert over all its tokens.
+Those depend only on the expert's own rows (x, dy and the row's combine
+weight), so the oracle computes them from a one-slot layer holding just that
+expert's rows with their weights, which keeps the check to a few seconds
+even where the expert has thousands of tokens (iso-width layer: about 3000).
 
 Bars (bf16 layers; derivation in test_gpu_backward): RMS(err) <= 2^-8 RMS
 over the sampled dx rows and combine-weight gradients, 2^-6 per dx row, 2^-7
@@ -78,14 +80,26 @@ def test_sampled_tokens(run):
     assert np.all(et <= 2.0 ** -6 * rt), f"{cfg.name}: dx rows {tok[et > 2.0 ** -6 * rt][:5]}"
 
 
+def oracle_expert_grads(cfg, inp, idx, w, dy, expert):
+    """The weight gradients of one expert: the oracle's backward of a layer
+    with one slot per token, over the tokens routed to `expert`, each with
+    the combine weight of the slot that names it (the shared expert, whose
+    gradients are not needed, is left out)."""
+    tok, slot = np.nonzero(idx == expert)
+    sub = dict(inp)
+    sub["x"] = inp["x"][tok]
+    sub["ws_gate"] = sub["ws_up"] = sub["ws_down"] = None
+    idx1 = np.full((tok.size, 1), expert, np.int32)
+    w1 = w[tok, slot].reshape(-1, 1).astype(np.float32)
+    return oracle.backward(sub, idx1, w1, dy[tok], cfg.score, cfg.renorm, 0.0, 0.0)
+
+
 @pytest.mark.timeout(900)
 def test_rare_expert_weight_grads(run):
     cfg, inp, idx, w, dy, got, rare, counts = run
     tok = np.nonzero((idx == rare).any(1))[0]
-    if tok.size > 256:
-        pytest.skip(f"{cfg.name}: the least loaded expert has {tok.size} tokens")
     print(f"{cfg.name}: expert {rare} with {tok.size} tokens", flush=True)
-    ref = oracle_on(cfg, inp, idx, w, dy, tok)
+    ref = oracle_expert_grads(cfg, inp, idx, w, dy, rare)
     bar = 2.0 * BF16_RMS if tok.size < 32 else BF16_RMS
     for name in ("dw_gate", "dw_up", "dw_down"):
         g, r = got[name].astype(np.float64), ref[name][rare]

@@ -60,6 +60,20 @@ CASES = [
     C("split_wide_f32", T=8200, d_model=192, n_experts=256, top_k=4, d_ff=64, dtype="f32", bias_range=0.05),
 ]
 
+# Wide-expert layers whose grouped GEMMs run the tile shapes of the large
+# workload layers (256-row tiles), compared on every output element: many
+# rows per expert (2048 on average, 2048 row tiles of 256), and a long K
+# (d_model 4096) with 256 rows per expert and the shared expert as a group; a Zipf-skewed router whose largest
+# group is most of the tokens beside experts with a few rows. The SwiGLU width
+# is large enough for the 2e-2 RMS(y) bar as well as the envelope.
+WIDE = [
+    C("tiles256_many_rows", T=8192, d_model=512, n_experts=32, top_k=8, d_ff=1024, score="sigmoid",
+      bias_range=0.1),
+    C("tiles256_long_k", T=2048, d_model=4096, n_experts=64, top_k=8, d_ff=2048, score="sigmoid", shared=True,
+      bias_range=0.1),
+    C("tiles256_zipf", T=8192, d_model=1024, n_experts=64, top_k=8, d_ff=768, zipf_s=1.1),
+]
+
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 def test_forward_matches_oracle(cfg):
@@ -69,6 +83,18 @@ def test_forward_matches_oracle(cfg):
     o = run_oracle(cfg, inp)
     assert_routing(g, o, cfg.name)
     check_y(cfg, inp, o, g["y"])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", WIDE, ids=lambda c: c.name)
+def test_wide_layers_every_element(cfg):
+    print(f"case {cfg.name}", flush=True)
+    inp, layer, x = setup(cfg)
+    g = gpu_forward(layer, x)
+    print(f"case {cfg.name}: oracle", flush=True)
+    o = run_oracle(cfg, inp)
+    assert_routing(g, o, cfg.name)
+    check_y(cfg, inp, o, g["y"], rms_bar=True)
 
 
 @pytest.mark.parametrize("cfg", CASES[:6], ids=lambda c: c.name)
