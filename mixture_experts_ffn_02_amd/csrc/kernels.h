@@ -138,6 +138,14 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in);
 // rows / kMinTileRows + groups entries.
 constexpr int kMinTileRows = 64;
 hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s);
+// bf16 forward products (gate/up with SwiGLU, or down) on 256 x 256 tiles of
+// eight waves (gemm8.hip): K % 64 == 0, N % 128 (gate/up) or N % 256 (down);
+// grouped launches take tile lists built with a row tile of 256.
+hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s);
+// Forward products with row tile bm: launch_gemm8 where bm is 256 and the
+// shape fits it, else launch_gemm.
+bool gemm8_fits(const GemmLaunch& g, int bm);
+hipError_t launch_gemm_fwd(const GemmLaunch& g, int bm, hipStream_t s);
 
 // --------------------------------------------------------------- backward
 hipError_t launch_to_bf16(int64_t n, const float* in, uint16_t* out, hipStream_t s);

@@ -232,7 +232,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
   gu.b_stream = stream_weights(lo.gemm_rows, n_groups, bm);
-  MOE_TRY(launch_gemm(gu, bm, s));
+  MOE_TRY(launch_gemm_fwd(gu, bm, s));
   mark(tm, MOE_PHASE_DOWN, s);
   GemmLaunch dn = gu;
   dn.gateup = false;
@@ -245,7 +245,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   dn.out = at<void>(ws, lo.yperm);
   dn.N = d;
   dn.K = L->d_ff;
-  MOE_TRY(launch_gemm(dn, bm, s));
+  MOE_TRY(launch_gemm_fwd(dn, bm, s));
 
   // shared expert: rows T*k .. T*k+T-1 of the grouped output, or its own GEMMs
   const float* shared_out = merged ? at<float>(ws, lo.yperm) + (size_t)T * k * d : nullptr;
@@ -263,7 +263,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sg.K = d;
     sg.rows = T;
     sg.b_stream = stream_weights(T, 1, bm_s);
-    MOE_TRY(launch_gemm(sg, bm_s, s));
+    MOE_TRY(launch_gemm_fwd(sg, bm_s, s));
   }
   mark(tm, MOE_PHASE_SHARED_DOWN, s);
   if (L->d_ff_shared > 0 && !merged) {
@@ -277,7 +277,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sd.K = L->d_ff_shared;
     sd.rows = T;
     sd.b_stream = stream_weights(T, 1, bm_s);
-    MOE_TRY(launch_gemm(sd, bm_s, s));
+    MOE_TRY(launch_gemm_fwd(sd, bm_s, s));
     shared_out = at<float>(ws, lo.ys);
   }
   mark(tm, MOE_PHASE_COMBINE, s);
@@ -848,7 +848,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   gu.max_m_tiles = max_tiles;
   gu.n_groups = n_groups;
   gu.b_stream = stream_weights(rows, n_groups, bm);
-  MOE_TRY(launch_gemm(gu, bm, s));
+  MOE_TRY(launch_gemm_fwd(gu, bm, s));
   GemmLaunch dn = gu;
   dn.gateup = false;
   dn.a = h;
@@ -857,7 +857,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   dn.out = out;
   dn.N = d_in;
   dn.K = d_ff;
-  MOE_TRY(launch_gemm(dn, bm, s));
+  MOE_TRY(launch_gemm_fwd(dn, bm, s));
   return MOE_OK;
 }
 
