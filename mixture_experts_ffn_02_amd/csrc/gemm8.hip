@@ -26,21 +26,32 @@
 //     SIMD reads LDS at about 25 bytes per clock, two at about 44, and a
 //     wave needs 6 KB per 8 MFMAs (256 cycles).
 //   * A stage is two 32 KB halves (A rows, weight rows) in a ring of five
-//     half-stage LDS buffers (160 KB). At the one barrier per stage (every
-//     wave has read stage t and its copies of stage t + 1 have landed) each
-//     wave copies its eighth of the weight half of stage t + 2 and of the A
-//     half of stage t + 3: the A rows, gathered token rows that mostly miss
-//     L2, are requested two stages ahead, the weight rows (shared by the
-//     tiles that run together on one XCD) one stage ahead.
+//     half-stage LDS buffers (160 KB). One barrier per stage: every wave has
+//     read stage t, and its copies of stage t + 1 have landed. Stage t's
+//     buffers are then free, and each wave spreads its eighth of the copies
+//     of the weight half of stage t + 2 and of the A half of stage t + 3 over
+//     the next four K steps, two 1 KB copies per step (issued all at once
+//     after the barrier, they stalled both waves of every SIMD together).
+//     The A rows, gathered token rows, are requested two stages ahead, the
+//     weight rows one stage ahead.
+//   * The copy stream runs on across the block's tiles: the last two stages
+//     of a tile copy the next tile's first stages, and the epilogue stores
+//     straight from the accumulators (buffer stores through a resource that
+//     spans the tile's rows, whose range check drops the rows past the
+//     tile's end), so no LDS is needed between tiles and the matrix cores
+//     never wait for a new tile's first stage.
 //   * Copies use global_load_lds_dwordx4 (lane i of a wave writes bytes
 //     16i..16i+15 of a 1 KB run of LDS rows); the 16-byte chunks of an LDS
 //     row are XOR-swizzled (applied on the global side) so that the
-//     fragment reads of 16 consecutive rows hit distinct banks.
+//     fragment reads of 16 consecutive rows hit distinct banks (measured: no
+//     bank conflicts).
 //   * Persistent grid, one block per CU, tiles split into 8 contiguous
-//     ranges, one per XCD (block b runs on XCD b % 8), each walked in raster
-//     groups of GM row tiles x all column tiles so the blocks resident on an
-//     XCD share weight and A stages in its L2. Row tiles come from the
-//     device-side tile list of the dispatch (group, m-tile).
+//     ranges, one per XCD (block b runs on XCD b % 8, measured), each walked
+//     in raster groups of GM row tiles x all column tiles so the blocks
+//     resident on an XCD share weight and A stages in its L2 (about 72% of
+//     the copies' requests hit L2 on the DeepSeek-style routed gate/up).
+//     Row tiles come from the device-side tile list of the dispatch (group,
+//     m-tile).
 #include <type_traits>
 
 #include "common.h"
@@ -55,9 +66,9 @@ constexpr int kSB = 128;              // bytes of one row in one stage
 constexpr int kKE = 64;               // K elements (bf16) per stage
 constexpr int kHalf = kBM * kSB;      // bytes of one operand's half-stage (32 KB)
 constexpr int kNH = 5;                // half-stage buffers
+// Every wave issues an eighth of each half-stage's copies (measured: leaving
+// the copies to the second wave of each SIMD alone was 6% slower).
 constexpr int kRuns = kHalf / 1024 / 8;  // 1 KB copies per wave per half-stage (4)
-constexpr int kScratch = 32 * (32 * 4 + 16);  // epilogue scratch per wave
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // XOR key of LDS row `row` (128-byte rows, 8 chunks): the 16 lanes of one
@@ -71,12 +82,13 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kSB + ((ch
 // (n a block-uniform multiple of kRuns) and its LDS reads done, then s_barrier, in
 // one asm block with a memory clobber so that no LDS access moves across.
 __device__ __forceinline__ void stage_barrier(int n) {
-  static_assert(kRuns == 4, "vmcnt immediates below assume 4 copies per half-stage");
-  if (n >= 3 * kRuns)
+  if (n >= 24)
+    asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (n >= 12)
     asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (n >= 2 * kRuns)
+  else if (n >= 8)
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (n >= kRuns)
+  else if (n >= 4)
     asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -90,10 +102,18 @@ __device__ __forceinline__ void interleave8() {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if (i < VM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read (copy)
+    // a global -> LDS copy: the scheduler classes it with LDS writes (0x200)
+    if (i < VM) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
   }
 }
+
+// One output tile of a launch: group e (grouped) or 0, rows row0 ..
+// row0 + rows - 1 of A and of the output, output columns from n0.
+struct Tile8 {
+  int64_t row0;
+  int e, rows, n0;
+};
 
 // STREAM: weight copies non-temporal (each weight tile read about once).
 template <bool GATEUP, bool GROUPED, bool STREAM>
@@ -112,7 +132,8 @@ void k_gemm8(GemmLaunch g) {
   const int64_t L0 = xcd * span;
   const int64_t L1 = L0 + span < total ? L0 + span : total;
   const size_t kbytes = (size_t)g.K * 2;
-  const int nk = g.K / kKE;
+  const int nk = g.K / kKE;  // >= 3 (launch_gemm8 checks)
+  const int nh = 2 * nk;     // half-stages of a tile
   const int group_m = g.group_m > 0 ? g.group_m : kGroupM;
   // Copy lanes: copy run R (= 8 i + wave, i < 4) of a half-stage writes LDS
   // rows 8R .. 8R + 7; lane l writes row 8R + l / 8, physical chunk l % 8,
@@ -126,218 +147,270 @@ void k_gemm8(GemmLaunch g) {
   for (int s4 = 0; s4 < 4; ++s4) loff[s4] = (uint32_t)swz(lane & 31, 2 * s4 + (lane >> 5));
   const int wrow0 = GATEUP ? wn * 32 : wn * 64;  // weight row of tile j = 0
   constexpr int kWStep = GATEUP ? 128 * kSB : 32 * kSB;  // tile j = 1 is this many bytes further
-  unsigned char* const scratch = lds + wave * kScratch;
+  // copy run R = 8 i + wave covers rows 8R .. 8R + 7 of a half-stage
+  constexpr int kSlots = 8;
+  const uint32_t b_lane = (uint32_t)((8 * wave + lrow) * kbytes) + lchunk * 16;
 
-  for (int64_t L = L0 + slot; L < L1; L += per_xcd) {
+  // The block's tiles, in raster order: 8 contiguous ranges of the order,
+  // one per XCD, each walked in groups of group_m row tiles x all column
+  // tiles; a tile of the device-side list naming no group, or with no rows,
+  // is skipped.
+  auto tile_at = [&](int64_t L, Tile8& t) -> bool {
     const int64_t gsz = (int64_t)group_m * n_tiles_n;
     const int64_t first_m = (L / gsz) * group_m;
     const int64_t gm = (m_tiles - first_m) < group_m ? (m_tiles - first_m) : group_m;
     const int64_t within = L % gsz;
     const int64_t tile_m = first_m + within % gm;
     const int tile_n = (int)(within / gm);
-
-    int e = 0;
-    int64_t row0;
-    int rows;
-    bool skip = false;
+    t.n0 = GATEUP ? tile_n * 128 : tile_n * 256;
     if constexpr (GROUPED) {
-      const int2 t = g.tiles[tile_m];
-      skip = t.x < 0 || t.x >= g.n_groups || t.y < 0;
-      e = skip ? 0 : t.x;
-      row0 = (int64_t)g.offsets[e] + (int64_t)t.y * kBM;
-      const int64_t left = (int64_t)g.offsets[e + 1] - row0;
-      rows = (int)(left < kBM ? left : kBM);
+      const int2 tl = g.tiles[tile_m];
+      if (tl.x < 0 || tl.x >= g.n_groups || tl.y < 0) return false;
+      t.e = tl.x;
+      t.row0 = (int64_t)g.offsets[t.e] + (int64_t)tl.y * kBM;
+      const int64_t left = (int64_t)g.offsets[t.e + 1] - t.row0;
+      t.rows = (int)(left < kBM ? left : kBM);
     } else {
-      row0 = tile_m * kBM;
-      const int64_t left = g.rows - row0;
-      rows = (int)(left < kBM ? left : kBM);
+      t.e = 0;
+      t.row0 = tile_m * kBM;
+      const int64_t left = g.rows - t.row0;
+      t.rows = (int)(left < kBM ? left : kBM);
     }
-    if (skip || rows <= 0) continue;  // uniform across the block
-    const bool xg = e == g.extra_group;
-    const unsigned char* A = reinterpret_cast<const unsigned char*>(g.a);
-    const unsigned char* B0 = xg ? reinterpret_cast<const unsigned char*>(g.bx0)
-                                 : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)e * g.N * kbytes;
-    const unsigned char* B1 = !GATEUP ? B0
-                              : xg    ? reinterpret_cast<const unsigned char*>(g.bx1)
-                                      : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)e * g.N * kbytes;
-    // gate/up: weight rows 0..127 of a stage are gate rows n0.., 128..255 up
-    // rows n0..; down: 256 weight rows n0..
-    const int n0 = GATEUP ? tile_n * 128 : tile_n * 256;
-
-    // Source rows of this lane's A copies: run 8 i + wave covers tile rows
-    // 64 i + 8 wave .. +7. Rows past the tile's end read a valid row; their
-    // results are never stored. Weight run 8 i + wave covers weight rows
-    // 64 i + 8 wave .. (gate/up: runs with i >= 2 are up rows 64 (i - 2)..),
-    // a block-uniform base plus one lane offset.
+    // the tile is block-uniform: say so, so that its values stay scalar
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(t.row0 >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)t.row0);
+    return t.rows > 0;
+  };
+  int64_t L = L0 + slot;
+  auto next_tile = [&](Tile8& t) -> bool {  // the next tile of this block from L on
+    for (; L < L1; L += per_xcd)
+      if (tile_at(L, t)) {
+        L += per_xcd;
+        return true;
+      }
+    return false;
+  };
+  // Per tile, for the copies: the source row of each of this lane's A runs
+  // (run 8 i + wave covers tile rows 64 i + 8 wave .. +7; rows past the
+  // tile's end read a valid row whose results are never stored) and the
+  // weight bases (gate/up: runs with i >= 2 are up rows).
+  struct Src {
     int32_t a_row[kRuns];
+    const unsigned char* b0;
+    const unsigned char* b1;
+  };
+  auto make_src = [&](const Tile8& t, Src& sr) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kRuns; ++i) {
-      int r = 64 * i + 8 * wave + lrow;
-      r = r < rows ? r : rows - 1;
-      int64_t src = row0 + r;
+      int r = 8 * (kSlots * i + wave) + lrow;
+      r = r < t.rows ? r : t.rows - 1;
+      int64_t src = t.row0 + r;
       if (g.a_rows) {
         src = g.a_rows[src];
         src = src < 0 ? 0 : (src >= g.a_row_count ? g.a_row_count - 1 : src);
       }
-      a_row[i] = (int32_t)src;
+      sr.a_row[i] = (int32_t)src;
     }
-    const uint32_t b_lane = (uint32_t)((8 * wave + lrow) * kbytes) + lchunk * 16;
-    // Copy of half-stage h (even: A rows of stage h / 2, odd: weight rows)
-    // into buffer h % 5.
-    auto issue = [&](int h) {
-      unsigned char* dst = lds + (h % kNH) * kHalf + wave * 1024;
-      const size_t koff = (size_t)(h >> 1) * kSB;
-      if ((h & 1) == 0) {
+    // block-uniform bases; the lane offset b_lane is added at the copy
+    const bool xg = t.e == g.extra_group;
+    sr.b0 = (xg ? reinterpret_cast<const unsigned char*>(g.bx0)
+                : reinterpret_cast<const unsigned char*>(g.b0) + (size_t)t.e * g.N * kbytes) +
+            (size_t)t.n0 * kbytes;
+    sr.b1 = GATEUP ? (xg ? reinterpret_cast<const unsigned char*>(g.bx1)
+                         : reinterpret_cast<const unsigned char*>(g.b1) + (size_t)t.e * g.N * kbytes) +
+                         (size_t)t.n0 * kbytes
+                   : sr.b0;
+  };
+  const unsigned char* const A = reinterpret_cast<const unsigned char*>(g.a);
+  // Copy runs I0 .. I0 + NR - 1 of half-stage h of the tile described by sr
+  // (even h: A rows of stage h / 2, odd: weight rows) into ring buffer `buf`.
+  auto issue_runs = [&](const Src& sr, int h, int buf, auto i0c, auto nc) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0c)::value, NR = decltype(nc)::value;
+    unsigned char* dst = lds + buf * kHalf + wave * 1024;
+    const size_t koff = (size_t)(h >> 1) * kSB;
+    if ((h & 1) == 0) {
 #pragma unroll
-        for (int i = 0; i < kRuns; ++i)
-          lds_dma16(A + (size_t)(uint32_t)a_row[i] * kbytes + koff + lchunk * 16, dst + i * 8192);
-        return;
-      }
-      auto wbase = [&](int i) {
-        return (GATEUP && i >= 2) ? B1 + (size_t)(n0 + 64 * (i - 2)) * kbytes + koff + b_lane
-                                  : B0 + (size_t)(n0 + 64 * i) * kbytes + koff + b_lane;
-      };
+      for (int i = I0; i < I0 + NR; ++i)
+        lds_dma16(A + (size_t)(uint32_t)sr.a_row[i] * kbytes + koff + lchunk * 16, dst + i * kSlots * 1024);
+      return;
+    }
+    // weight run i starts at weight row 8 kSlots i (gate/up: the second half
+    // of the runs are up rows)
 #pragma unroll
-      for (int i = 0; i < kRuns; ++i) lds_dma16<STREAM>(wbase(i), dst + i * 8192);
-    };
+    for (int i = I0; i < I0 + NR; ++i) {
+      const unsigned char* src = (GATEUP && i >= kRuns / 2)
+                                     ? sr.b1 + (size_t)(8 * kSlots * (i - kRuns / 2)) * kbytes + koff + b_lane
+                                     : sr.b0 + (size_t)(8 * kSlots * i) * kbytes + koff + b_lane;
+      lds_dma16<STREAM>(src, dst + i * kSlots * 1024);
+    }
+  };
+  using R0 = std::integral_constant<int, 0>;
+  using R2 = std::integral_constant<int, kRuns / 2>;   // half of a half-stage's runs
+  using R4 = std::integral_constant<int, kRuns>;
 
-    f32x16 acc[4][2];
+  Tile8 cur, nxt;
+  if (!next_tile(cur)) return;
+  Src sc, sn;
+  make_src(cur, sc);
+  bool has_next = next_tile(nxt);
+  if (has_next) make_src(nxt, sn);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
+
+  // Fragments of one K step: A tiles i (rows 128 wm + 32 i + lane % 32)
+  // and weight tiles j (rows wrow0 + lane % 32, and kWStep further).
+  struct Frag {
+    u32x4 a[4], b[2];
+  };
+  auto load_frag = [&](Frag& f, int abuf, int bbuf, int s4) __attribute__((always_inline)) {
+    const unsigned char* ab = lds + abuf * kHalf + wm * 128 * kSB + loff[s4];
+    const unsigned char* bb = lds + bbuf * kHalf + wrow0 * kSB + loff[s4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const u32x4*>(ab + i * 32 * kSB);
+    f.b[0] = *reinterpret_cast<const u32x4*>(bb);
+    f.b[1] = *reinterpret_cast<const u32x4*>(bb + kWStep);
+  };
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
+                                                            __builtin_bit_cast(bf16x8, f.b[j]), acc[i][j], 0, 0, 0);
+  };
+
+  // Epilogue of a finished tile straight from the accumulators (no LDS, so
+  // it overlaps the next tile's copies): element x of a 32 x 32 tile sits in
+  // row 8(x/4) + 4(l/32) + x%4, column l % 32 of lane l, so each store
+  // writes 32 consecutive columns of two rows. gate/up: H = silu(g) u in
+  // bf16; down: fp32. Buffer stores through a resource that spans exactly
+  // the tile's rows, so the hardware range check drops the rows past the
+  // tile's end, and every address is one 32-bit lane offset plus a constant.
+  auto epilogue = [&](const Tile8& t) __attribute__((always_inline)) {
+    constexpr int EB = GATEUP ? 2 : 4;
+    unsigned char* const obase = reinterpret_cast<unsigned char*>(g.out) + (size_t)t.row0 * g.N * EB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, t.rows * g.N * EB, 0x00020000);
+    const int col = (GATEUP ? t.n0 + wn * 32 : t.n0 + wn * 64) + (lane & 31);
+    const int lane_off = ((wm * 128 + 4 * (lane >> 5)) * g.N + col) * EB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int off = lane_off + (i * 32 + 8 * (x >> 2) + (x & 3)) * g.N * EB;
+        if constexpr (GATEUP) {
+          const float gv = acc[i][0][x], uv = acc[i][1][x];
+          const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rs, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][0][x]), rs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][1][x]), rs, off + 32 * 4, 0, 0);
+        }
+      }
+    }
+  };
+
+  // The copy stream. Half-stage q of the block counts the half-stages of all
+  // its tiles in order (q = tile's first q + h); it lives in ring buffer
+  // q % 5. Over the four K steps that follow the barrier of stage t (whose
+  // buffers it frees) each wave issues its eighth of half-stage 2t + 5 (the
+  // weight half of stage t + 2; runs 0-1, then 2-3) and 2t + 6 (the A half of
+  // stage t + 3; runs 0-1, 2-3): in stage t that is half-stage 2t + 3 runs
+  // 2-3 in step 0, 2t + 4 in steps 1-2, 2t + 5 runs 0-1 in step 3.
+  // Half-stages past the tile's end belong to the next tile: with nk >= 3
+  // they occur only in stages nk - 2 (2t + 4, 2t + 5) and nk - 1 (all). The
+  // block's very first tile copies half-stages 0 .. 4 up front.
+  int qbase = 0;  // ring position of the current tile's half-stage 0
+  enum { kNone = 0, kCur = 1, kNext = 2 };
+  // copy of half-stage h (current tile's numbering) for slot owner w
+  auto issue_q = [&](int w, int h, auto i0c, auto nc) __attribute__((always_inline)) {
+    if (w == kCur)
+      issue_runs(sc, h, (qbase + h) % kNH, i0c, nc);
+    else if (w == kNext)
+      issue_runs(sn, h - nh, (qbase + h) % kNH, i0c, nc);
+  };
+  for (int h = 0; h < kNH; ++h) issue_runs(sc, h, h, R0{}, R4{});
+  stage_barrier(kRuns * (kNH - 2));  // stage 0 landed; three halves may be in flight
+  Frag P, Q;
+  load_frag(P, qbase % kNH, (qbase + 1) % kNH, 0);
+  // Stage t. STEADY: every copy belongs to the current tile and the next
+  // stage exists (one basic block per K step, so the scheduler interleaves
+  // the copies, reads and MFMAs). Otherwise the copy slots w0 (step 0),
+  // w12 (steps 1-2), w3 (step 3) name the tile each copy belongs to (or
+  // none); `more`: the stage after it exists (its first fragments are read
+  // in step 3); `inflight`: the A half of stage t + 2 exists, so the
+  // barrier lets its copies stay in flight.
+  auto stage = [&](int t, auto steady, int w0, int w12, int w3, bool more, bool inflight)
+      __attribute__((always_inline)) {
+    constexpr bool S = decltype(steady)::value;
+    const int abuf = (qbase + 2 * t) % kNH, bbuf = (qbase + 2 * t + 1) % kNH;
+    const int na = (abuf + 2) % kNH, nb = (bbuf + 2) % kNH;
+    load_frag(Q, abuf, bbuf, 1);
+    if (S) issue_runs(sc, 2 * t + 3, (qbase + 2 * t + 3) % kNH, R2{}, R2{});
+    else issue_q(w0, 2 * t + 3, R2{}, R2{});
+    mma(P);
+    interleave8<6, kRuns / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(P, abuf, bbuf, 2);
+    if (S) issue_runs(sc, 2 * t + 4, (qbase + 2 * t + 4) % kNH, R0{}, R2{});
+    else issue_q(w12, 2 * t + 4, R0{}, R2{});
+    mma(Q);
+    interleave8<6, kRuns / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(Q, abuf, bbuf, 3);
+    if (S) issue_runs(sc, 2 * t + 4, (qbase + 2 * t + 4) % kNH, R2{}, R2{});
+    else issue_q(w12, 2 * t + 4, R2{}, R2{});
+    mma(P);
+    interleave8<6, kRuns / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    // stage barrier: this wave's copies of stage t + 1 have landed (the A
+    // half of stage t + 2, issued after them, may still be in flight) and
+    // every wave has read stage t
+    stage_barrier(S || inflight ? kRuns : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (S) issue_runs(sc, 2 * t + 5, (qbase + 2 * t + 5) % kNH, R0{}, R2{});
+    else issue_q(w3, 2 * t + 5, R0{}, R2{});
+    if (S || more) load_frag(P, na, nb, 0);
+    mma(Q);
+    interleave8<6, kRuns / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Steady = std::true_type;
+  using Generic = std::false_type;
+  bool first = true;
+  while (true) {
+    int t = 0;
+    if (first) {  // half-stages 3 and 4 were copied up front
+      stage(0, Generic{}, kNone, kNone, kCur, true, true);
+      t = 1;
+    }
+    for (; t < nk - 2; ++t) stage(t, Steady{}, 0, 0, 0, true, true);
+    const int wn_ = has_next ? kNext : kNone;
+    stage(nk - 2, Generic{}, kCur, wn_, wn_, true, has_next);
+    stage(nk - 1, Generic{}, wn_, wn_, wn_, has_next, has_next);
+    epilogue(cur);
+    if (!has_next) break;
+    // the next tile becomes current; its first stages are already in flight
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
-
-    // Fragments of one K step: A tiles i (rows 128 wm + 32 i + lane % 32)
-    // and weight tiles j (rows wrow0 + lane % 32, and kWStep further).
-    struct Frag {
-      u32x4 a[4], b[2];
-    };
-    auto load_frag = [&](Frag& f, uint32_t abuf, uint32_t bbuf, int s4) {
-      const unsigned char* ab = lds + abuf + wm * 128 * kSB + loff[s4];
-      const unsigned char* bb = lds + bbuf + wrow0 * kSB + loff[s4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const u32x4*>(ab + i * 32 * kSB);
-      f.b[0] = *reinterpret_cast<const u32x4*>(bb);
-      f.b[1] = *reinterpret_cast<const u32x4*>(bb + kWStep);
-    };
-    auto mma = [&](const Frag& f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
-                                                              __builtin_bit_cast(bf16x8, f.b[j]), acc[i][j], 0, 0, 0);
-    };
-
-    // Prologue: half-stages 0..4 (stages 0 and 1, the A half of stage 2).
-    const int nh = 2 * nk;
-    const int pro = nh < kNH ? nh : kNH;
-    for (int h = 0; h < pro; ++h) issue(h);
-    stage_barrier((pro - 2) * kRuns);  // stage 0 landed; the later halves may be in flight
-    Frag P, Q;
-    uint32_t abuf = 0, bbuf = kHalf;  // ring offsets of stage t's halves ((2t) % 5, (2t + 1) % 5)
-    // One stage: K steps 0..2 with the next step's fragment reads between
-    // the MFMAs; the stage barrier (this wave's copies of stage t + 1 have
-    // landed, the A half of stage t + 2 issued after them may still be in
-    // flight, and every wave has read stage t); then, stage t's buffers
-    // being free, the copies of the weight half of stage t + 2 and the A
-    // half of stage t + 3, the reads of step 0 of stage t + 1 and the MFMAs
-    // of step 3. FULL: all of those exist (t + 3 < nk), so the last step is
-    // one basic block the scheduler can interleave.
-    auto stage = [&](int t, auto full) {
-      load_frag(Q, abuf, bbuf, 1);
-      mma(P);
-      interleave8<6, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      load_frag(P, abuf, bbuf, 2);
-      mma(Q);
-      interleave8<6, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      load_frag(Q, abuf, bbuf, 3);
-      mma(P);
-      interleave8<6, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      const uint32_t na = abuf + 2 * kHalf >= kNH * kHalf ? abuf + 2 * kHalf - kNH * kHalf : abuf + 2 * kHalf;
-      const uint32_t nb = bbuf + 2 * kHalf >= kNH * kHalf ? bbuf + 2 * kHalf - kNH * kHalf : bbuf + 2 * kHalf;
-      if constexpr (decltype(full)::value) {
-        stage_barrier(kRuns);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(2 * t + 5);
-        issue(2 * t + 6);
-        load_frag(P, na, nb, 0);
-        mma(Q);
-        interleave8<6, 8>();
-      } else {
-        stage_barrier(2 * t + 4 < nh ? kRuns : 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (2 * t + 5 < nh) issue(2 * t + 5);
-        if (2 * t + 6 < nh) issue(2 * t + 6);
-        if (t + 1 < nk) load_frag(P, na, nb, 0);
-        mma(Q);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      abuf = na;
-      bbuf = nb;
-    };
-    load_frag(P, abuf, bbuf, 0);
-    int t = 0;
-    for (; t + 3 < nk; ++t) stage(t, std::true_type{});
-    for (; t < nk; ++t) stage(t, std::false_type{});
-    barrier();  // every wave is done with the stage buffers
-
-    // Epilogue of this wave's 4 x 2 accumulator tiles (gate/up: 4 tiles of
-    // H, SwiGLU applied; down: 8 fp32 tiles). A 32 x 32 tile goes through
-    // the wave's scratch (row-major, padded rows) and leaves as 16-byte row
-    // chunks. Element x of a tile sits in row 8(x/4) + 4(l/32) + x%4, column
-    // l % 32 of lane l.
-    auto put_tile = [&](auto zero, const f32x16& v, int i, int col0) {
-      using T = decltype(zero);
-      constexpr int EB = (int)sizeof(T), P2 = 32 * EB + 16, CH = 32 * EB / 16;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int r = 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-        T o;
-        if constexpr (sizeof(T) == 2)
-          o = f32_to_bf16(v[x]);
-        else
-          o = v[x];
-        *reinterpret_cast<T*>(scratch + r * P2 + (lane & 31) * EB) = o;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // tile base (block-uniform) plus a 32-bit offset: m < 256 rows
-      unsigned char* obase = reinterpret_cast<unsigned char*>(g.out) + (size_t)row0 * g.N * EB;
-#pragma unroll
-      for (int q0 = 0; q0 < 32 * CH; q0 += 64) {
-        const int qq = q0 + lane, r = qq / CH, c16 = qq % CH;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(scratch + r * P2 + c16 * 16);
-        const int m = wm * 128 + i * 32 + r;
-        if (m < rows) *reinterpret_cast<u32x4*>(obase + (uint32_t)((m * g.N + col0 + c16 * (16 / EB)) * EB)) = val;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (GATEUP) {
-        f32x16 hv;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float gv = acc[i][0][x], uv = acc[i][1][x];
-          hv[x] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        }
-        put_tile(uint16_t{}, hv, i, n0 + wn * 32);
-      } else {
-        put_tile(float{}, acc[i][0], i, n0 + wn * 64);
-        put_tile(float{}, acc[i][1], i, n0 + wn * 64 + 32);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    barrier();  // scratch reads done before the next tile's copies
+    qbase = (qbase + nh) % kNH;
+    cur = nxt;
+    sc = sn;
+    has_next = next_tile(nxt);
+    if (has_next) make_src(nxt, sn);
+    first = false;
   }
 }
 
@@ -346,7 +419,7 @@ void k_gemm8(GemmLaunch g) {
 // 256 x 256 eight-wave tiles for bf16 forward products; the caller checks
 // dtype, K % 64 and N (gate/up: % 128, down: % 256).
 hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
-  if (g.dtype != 1 || g.K % kKE || (g.gateup ? g.N % 128 : g.N % 256) || g.bt || g.koffs || g.out_g)
+  if (g.dtype != 1 || g.K % kKE || g.K < 3 * kKE || (g.gateup ? g.N % 128 : g.N % 256) || g.bt || g.koffs || g.out_g)
     return hipErrorInvalidValue;
   int64_t blocks = cu_count();
   blocks = (blocks + kXcd - 1) / kXcd * kXcd;
@@ -357,7 +430,7 @@ hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
     blocks = need < blocks ? need : blocks;
   }
   const dim3 grid((unsigned)blocks), block(512);
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, g); };
+  auto go = [&](auto kern) __attribute__((always_inline)) { hipLaunchKernelGGL(kern, grid, block, 0, s, g); };
   if (g.gateup) {
     if (g.offsets) {
       if (g.b_stream) go(k_gemm8<true, true, true>); else go(k_gemm8<true, true, false>);
@@ -381,7 +454,8 @@ hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
 #define MOE_GEMM8 1
 #endif
 bool gemm8_fits(const GemmLaunch& g, int bm) {
-  return MOE_GEMM8 && bm == 256 && g.dtype == 1 && g.K % kKE == 0 && (g.gateup ? g.N % 128 == 0 : g.N % 256 == 0) &&
+  return MOE_GEMM8 && bm == 256 && g.dtype == 1 && g.K % kKE == 0 && g.K >= 3 * kKE &&
+         (g.gateup ? g.N % 128 == 0 : g.N % 256 == 0) &&
          !g.bt && !g.koffs && !g.out_g;
 }
 
