@@ -241,6 +241,27 @@ moe_status moe_forward_ex(const moe_layer *layer, const void *x, int64_t T, cons
                           int32_t *topk_idx, float *topk_w, int32_t *counts, void *ws, size_t ws_bytes,
                           void *stream, moe_timing *timing);
 
+/*
+ * moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results as moe_forward, with the scratch space
+ * taken from a fixed array inside the library instead of a caller
+ * workspace. The caller still passes x, y and the optional topk_idx,
+ * topk_w and counts. No hipMalloc, hipFree or other allocation happens in
+ * the call.
+ *   - The array holds MOE_NOALLOC_BYTES (256 MiB) per GPU, from the first
+ *     call on that GPU until the process ends. A layer and T whose
+ *     moe_workspace_size exceeds it return MOE_ERR_WORKSPACE before anything
+ *     is enqueued (for example: the 640-wide 16-expert layer up to 8192
+ *     tokens fits; a 7168-wide 256-expert layer up to about 900).
+ *   - Every call on one GPU uses that GPU's one array, whose contents persist
+ *     from call to call: calls that overlap on one GPU (other streams,
+ *     other host threads) race and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_BYTES ((size_t)256 << 20)
+moe_status moe_forward_noalloc(const moe_layer *layer, const void *x, int64_t T, float *y, int32_t *topk_idx,
+                               float *topk_w, int32_t *counts, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Backward pass (training)                                                */
 /* ---------------------------------------------------------------------- */

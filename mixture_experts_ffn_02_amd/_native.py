@@ -24,7 +24,10 @@ EXPORTS = (
     "moe_status_str", "moe_workspace_size", "moe_route", "moe_route_ex", "moe_bias_update", "moe_permute",
     "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_forward_ex",
     "moe_timing_create", "moe_timing_destroy", "moe_timing_read", "moe_timing_select", "moe_backward_workspace_size", "moe_backward",
+    "moe_forward_noalloc",
 )
+# Bytes of the library's fixed scratch array used by moe_forward_noalloc.
+MOE_NOALLOC_BYTES = 256 << 20
 
 
 class MoeError(RuntimeError):
@@ -81,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.moe_timing_create.argtypes = [P(vp)]
     L.moe_timing_destroy.argtypes = [vp]
     L.moe_forward_ex.argtypes = [LP, vp, i64, OP, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.moe_forward_noalloc.argtypes = [LP, vp, i64, vp, vp, vp, vp, vp]
     L.moe_timing_read.argtypes = [vp, P(ctypes.c_float)]
     L.moe_timing_select.argtypes = [vp, ctypes.c_uint32]
     L.moe_backward_workspace_size.argtypes = [LP, i64, P(sz)]

@@ -3,6 +3,7 @@
 // of every entry point are in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -877,6 +878,48 @@ moe_status moe_combine(const moe_layer* L, int64_t T, const float* y_perm, const
 moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(L, x, T, nullptr, y, topk_idx, topk_w, counts, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+// Scratch of moe_forward_noalloc: one array per GPU, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not device
+// memory: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// used for every launch.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (null on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+moe_status moe_forward_noalloc(const moe_layer* L, const void* x, int64_t T, float* y, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, void* stream) {
+  size_t need = 0;
+  moe_status st = moe_workspace_size(L, T, &need);
+  if (st != MOE_OK) return st;
+  if (need > MOE_NOALLOC_BYTES) return MOE_ERR_WORKSPACE;
+  if (T == 0) return forward_impl(L, x, T, nullptr, y, topk_idx, topk_w, counts, nullptr, 0, (hipStream_t)stream,
+                                  nullptr);
+  // forward_impl reads no workspace byte it has not written in the same
+  // call, so what earlier calls left in the array needs no clearing
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_HIP;
+  return forward_impl(L, x, T, nullptr, y, topk_idx, topk_w, counts, ws, MOE_NOALLOC_BYTES, (hipStream_t)stream,
+                      nullptr);
 }
 
 moe_status moe_forward_ex(const moe_layer* L, const void* x, int64_t T, const moe_route_opts* opts, float* y,
