@@ -131,6 +131,50 @@ def phase_bytes_and_flops(cfg):
     return work
 
 
+def gemm_row_tile(rows: int, groups: int, n: int, d_in: int, cu: int = 256) -> int:
+    """The library's row tile for a bf16 grouped launch (host rule of
+    gemm.hip: 64 for few rows per group, 256 for many rows or a long K)."""
+    avg = rows // max(groups, 1)
+    busy = min(groups, rows)
+    if avg <= 128 and busy * (n // 128 if n % 128 == 0 else n // 64) >= 2 * cu:
+        return 64
+    long_k = d_in >= 4096
+    return 256 if (avg >= 768 or long_k) and (rows // 256) * (n // 128) >= 4 * cu else 128
+
+
+def gateup_kernel(cfg) -> str:
+    merged = shared_as_group(cfg)
+    rows = cfg.T * cfg.top_k + (cfg.T if merged else 0)
+    groups = cfg.n_experts + (1 if merged else 0)
+    if cfg.dtype == "bf16" and gemm_row_tile(rows, groups, cfg.d_ff, cfg.d_model) == 256 and cfg.d_ff % 128 == 0:
+        return "k_gemm8<gate/up, grouped> (256 x 256 tiles, eight waves)"
+    return f"k_gemm<{cfg.dtype}, gate/up, grouped>"
+
+
+def measure_permute(cfg, layer, x, reps: int):
+    """moe_permute with the permuted copy of x (x_perm), which moe_forward
+    itself never writes (its gate/up GEMM gathers the rows): ms per call and
+    algorithmic bytes: x read once, T*k rows written, ids read and row ids
+    written (int32 each)."""
+    import torch
+
+    idx = layer.route(x)["idx"]
+    layer.permute(x, idx)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        layer.permute(x, idx)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    eb = 2 if cfg.dtype == "bf16" else 4
+    by = cfg.T * cfg.d_model * eb * (1 + cfg.top_k) + cfg.T * cfg.top_k * 8
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bytes": by, "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "moe_permute writing x_perm (not part of moe_forward, whose GEMM gathers the rows)"}
+
+
 def measure_backward(cfg, layer, x, steps: int, warmup: int):
     """moe_backward for the forward's routing and a seeded dy: ms per call
     (HIP events on the layer's stream) and its algorithmic expert-GEMM work:
@@ -271,7 +315,7 @@ def main():
     gu = work["gateup"]["flops"] / (gateup_ms * 1e-3) / 1e12
     traffic = traffic_from_profile("gateup", args.workload)
     what = "routed experts + the shared expert as one more group" if shared_as_group(cfg) else "routed experts"
-    roofline = {"bound": "mfma", "kernel": f"k_gemm<{cfg.dtype}, gate/up, grouped> ({what})",
+    roofline = {"bound": "mfma", "kernel": f"{gateup_kernel(cfg)} ({what})",
                 "achieved": round(gu, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
     def phase_detail(pms):
@@ -325,6 +369,7 @@ def main():
         out["phases_cold"]["ms_per_step"] = round(sum(cold.values()), 4)
         out["phases_cold"]["note"] = (f"{args.cold_steps} steps, each after a {FLUSH_BYTES >> 20} MiB device copy "
                                       "outside the timed events (L2 and the last-level cache evicted)")
+    out["permute"] = measure_permute(cfg, layer, x, max(3, min(args.steps, 20)))
     # expert weights the step had to read: experts that received tokens (+ the shared one)
     counts = layer.route(x)["counts"].cpu().numpy()
     used = int((counts > 0).sum())

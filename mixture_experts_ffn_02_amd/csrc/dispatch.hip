@@ -197,8 +197,14 @@ __global__ __launch_bounds__(kScanThreads) void k_tiles_from_offsets(const int32
 }
 
 // One wave per token: rows of its k slots, the inverse map, and optionally
-// the copy of x[t] into its k rows of x_perm (the row is fetched from HBM
-// once; the k-1 further reads of it hit the cache).
+// the copy of x[t] into its k rows of x_perm. The row is read from HBM once,
+// into registers (16 KB of it per pass, 16 bytes per lane per load, all in
+// flight together), and each pass is then stored to the k rows with
+// non-temporal stores (x_perm is written once and not read back here).
+// Measured against a loop that re-read the row for every slot: 3.5 -> 5.2
+// TB/s at the DeepSeek-style layer (2.43 -> 1.61 ms), 3.4 -> 4.9 TB/s at the
+// Qwen3-like one; the non-temporal stores give 5-14% of that over plain ones.
+constexpr int kPermPass = 16;  // 16-byte chunks per lane per pass
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
                                                  const int32_t* __restrict__ base, int64_t T, int k, int E, int tpb,
                                                  int32_t* __restrict__ row_of, int32_t* __restrict__ tok_of_row,
@@ -220,11 +226,23 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
   if (!x_perm) return;
   const int nchunk = row_bytes >> 4;
   const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * row_bytes);
-  for (int j = 0; j < k; ++j) {
-    const int r = __shfl(my_row, j);  // every lane of the wave is active here
-    if (r < 0) continue;
-    u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (size_t)r * row_bytes);
-    for (int c = lane; c < nchunk; c += 64) dst[c] = src[c];
+  for (int c0 = 0; c0 < nchunk; c0 += 64 * kPermPass) {
+    u32x4 v[kPermPass];
+#pragma unroll
+    for (int i = 0; i < kPermPass; ++i) {
+      const int c = c0 + 64 * i + lane;
+      if (c < nchunk) v[i] = src[c];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = __shfl(my_row, j);  // every lane of the wave is active here
+      if (r < 0) continue;
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (size_t)r * row_bytes);
+#pragma unroll
+      for (int i = 0; i < kPermPass; ++i) {
+        const int c = c0 + 64 * i + lane;
+        if (c < nchunk) __builtin_nontemporal_store(v[i], dst + c);
+      }
+    }
   }
 }
 

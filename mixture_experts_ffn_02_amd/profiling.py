@@ -9,7 +9,12 @@ both in KiB per dispatch), scaled by what the same counters read for a plain
 device-to-device copy of known size that ran in the same process:
 
     python -m mixture_experts_ffn_02_amd.profiling traffic --fetch DIR1 --write DIR2 \\
-        --kernel "k_gemm<unsigned short, true, true" --copy-bytes 268435456 --cmd "..."
+        --kernel "k_gemm8<true, true" --copy-bytes 268435456 --cmd "..."
+
+Matrix-core use of the GEMM launches from one counter run (SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE):
+
+    python -m mixture_experts_ffn_02_amd.profiling mfma DIR --cmd "..."
 
 Both print a summary to stdout; the traffic summary carries the hash of the
 kernel source it was measured on, so that stale numbers can be recognised.
@@ -25,7 +30,8 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SOURCES = ["mixture_experts_ffn_02_amd/csrc/gemm.hip", "mixture_experts_ffn_02_amd/csrc/moe_api.cpp"]
+GEMM_SOURCES = ["mixture_experts_ffn_02_amd/csrc/gemm.hip", "mixture_experts_ffn_02_amd/csrc/gemm8.hip",
+                "mixture_experts_ffn_02_amd/csrc/moe_api.cpp"]
 
 
 def source_hash(paths=GEMM_SOURCES) -> str:
@@ -70,22 +76,28 @@ def traffic(args) -> None:
     fetch = _counter(args.fetch, "FETCH_SIZE")
     write = _counter(args.write, "WRITE_SIZE")
 
-    def pick(table, key):
+    def pick(table, key, large=False):
         vals = [v for k, vs in table.items() if key in k for v in vs]
         if not vals:
             raise SystemExit(f"kernel matching {key!r} not found")
+        if large:  # the dispatches of the kind that moves data (see --large)
+            vals = [v for v in vals if v >= 0.5 * max(vals)]
         return statistics.mean(vals), len(vals)
 
     copy_kib = args.copy_bytes / 1024.0
     cf, _ = pick(fetch, args.copy_kernel)
     cw, _ = pick(write, args.copy_kernel)
-    kf, n = pick(fetch, args.kernel)
-    kw, _ = pick(write, args.kernel)
+    kf, n = pick(fetch, args.kernel, args.large)
+    kw, _ = pick(write, args.kernel, args.large)
     sf, sw = copy_kib / cf, copy_kib / cw
     total = (kf * sf + kw * sw) * 1024.0
-    print("# HBM traffic of one kernel from rocprofv3 counters")
+    print("# HBM traffic of one kernel from rocprofv3 counters (bytes that leave L2 for memory)")
     print(f"# command (FETCH_SIZE run): {args.cmd.replace('COUNTER', 'FETCH_SIZE')}")
     print(f"# command (WRITE_SIZE run): {args.cmd.replace('COUNTER', 'WRITE_SIZE')}")
+    print("# scale: the counters of a plain elementwise copy (torch.mul by 1.0, 16 bytes per lane) of copy_bytes")
+    print("# run in the same process")
+    if args.note:
+        print(f"# {args.note}")
     print(f"kernel: {args.kernel}")
     print(f"dispatches: {n}")
     print(f"fetch_kib_per_dispatch: {kf:.1f}")
@@ -95,19 +107,54 @@ def traffic(args) -> None:
     print(f"copy_write_kib: {cw:.1f}")
     print(f"fetch_scale: {sf:.4f}")
     print(f"write_scale: {sw:.4f}")
+    print(f"read_bytes_per_launch: {kf * sf * 1024.0:.0f}")
+    print(f"write_bytes_per_launch: {kw * sw * 1024.0:.0f}")
     print(f"hbm_bytes_per_launch: {total:.0f}")
+    if args.algorithmic:
+        print(f"algorithmic_bytes_per_launch: {args.algorithmic:.0f}")
+        print(f"traffic_over_algorithmic: {total / args.algorithmic:.3f}")
     if args.rdreq:
         rq = _counter(args.rdreq, "TCC_EA0_RDREQ_128B_sum")
         r6 = _counter(args.rdreq, "TCC_EA0_RDREQ_64B_sum")
-        k128, _ = pick(rq, args.kernel)
-        k64, _ = pick(r6, args.kernel)
+        r3 = _counter(args.rdreq, "TCC_EA0_RDREQ_32B_sum")
+        k128, _ = pick(rq, args.kernel, args.large)
+        k64, _ = pick(r6, args.kernel, args.large)
+        k32, _ = pick(r3, args.kernel, args.large)
         c128, _ = pick(rq, args.copy_kernel)
         c64, _ = pick(r6, args.copy_kernel)
-        print(f"# cross-check: EA read requests by size (128 B and 64 B); command: "
+        c32, _ = pick(r3, args.copy_kernel)
+        kb = 128 * k128 + 64 * k64 + 32 * k32
+        cb = 128 * c128 + 64 * c64 + 32 * c32
+        print(f"# cross-check: read requests to memory by size (32, 64 and 128 bytes); command: "
               f"{args.cmd.replace('COUNTER', 'TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum')}")
-        print(f"rdreq_bytes_per_dispatch: {128 * k128 + 64 * k64:.0f}")
-        print(f"copy_rdreq_bytes: {128 * c128 + 64 * c64:.0f}")
+        print(f"rdreq_bytes_per_dispatch: {kb:.0f}")
+        print(f"copy_rdreq_bytes: {cb:.0f}")
+        print(f"rdreq_over_scaled_fetch: {kb / (kf * sf * 1024.0):.4f}")
     print(f"source_sha256: {source_hash()}")
+
+
+def mfma(args) -> None:
+    """Matrix-core use of every launch of the kernels matching --kernel:
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) over GRBM_GUI_ACTIVE
+    (summed over the XCDs, so divided by their count) times the SIMD count,
+    and the bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512 flops)."""
+    busy = _counter(args.dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = _counter(args.dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gui = _counter(args.dir, "GRBM_GUI_ACTIVE")
+    print("# matrix-core use from rocprofv3 counters")
+    print(f"# command: {args.cmd}")
+    print(f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} * {args.simds}); "
+          f"flops = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    print(f"{'launches':>8} {'mfma_busy':>9} {'gflop':>10} {'cycles':>12}  kernel")
+    for name in busy:
+        if not any(k in name for k in args.kernel):
+            continue
+        b = statistics.mean(busy[name])
+        m = statistics.mean(mops.get(name, [0.0]))
+        g = statistics.mean(gui.get(name, [0.0])) / args.xcds
+        util = b / (g * args.simds) if g else 0.0
+        short = name.replace("moe::(anonymous namespace)::", "")[:90]
+        print(f"{len(busy[name]):8d} {util:9.3f} {m * 512 / 1e9:10.1f} {g:12.0f}  {short}")
 
 
 def main(argv=None) -> None:
@@ -120,12 +167,23 @@ def main(argv=None) -> None:
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
     b.add_argument("--kernel", required=True)
-    b.add_argument("--copy-kernel", default="vectorized_elementwise_kernel")
+    b.add_argument("--copy-kernel", default="MulFunctor<float>")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--rdreq", default=None, help="optional run with TCC_EA0_RDREQ_{128B,64B}_sum")
+    b.add_argument("--large", action="store_true",
+                   help="average only the dispatches reading at least half the largest value (a kernel launched "
+                        "both with and without a data-moving option)")
+    b.add_argument("--algorithmic", type=float, default=0.0, help="algorithmic bytes per launch, for the ratio")
+    b.add_argument("--note", default="")
     b.add_argument("--cmd", required=True)
+    c = sub.add_parser("mfma")
+    c.add_argument("dir")
+    c.add_argument("--kernel", nargs="+", default=["k_gemm"])
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("--cmd", required=True)
     args = ap.parse_args(argv)
-    {"stats": stats, "traffic": traffic}[args.what](args)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[args.what](args)
 
 
 if __name__ == "__main__":
