@@ -16,7 +16,7 @@ SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE):
 
     python -m mixture_experts_ffn_02_amd.profiling mfma DIR --cmd "..."
 
-Both print a summary to stdout; the traffic summary carries the hash of the
+Each prints a summary to stdout; the traffic summary carries the hash of the
 kernel source it was measured on, so that stale numbers can be recognised.
 """
 from __future__ import annotations
@@ -123,38 +123,61 @@ def traffic(args) -> None:
         c128, _ = pick(rq, args.copy_kernel)
         c64, _ = pick(r6, args.copy_kernel)
         c32, _ = pick(r3, args.copy_kernel)
+        rq_cmd = args.cmd.replace("--pmc COUNTER", "--pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum "
+                                  "TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum").replace("COUNTER", "TCC_EA0_RDREQ")
         kb = 128 * k128 + 64 * k64 + 32 * k32
         cb = 128 * c128 + 64 * c64 + 32 * c32
         print(f"# cross-check: read requests to memory by size (32, 64 and 128 bytes); command: "
-              f"{args.cmd.replace('COUNTER', 'TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum')}")
+              f"{rq_cmd}")
         print(f"rdreq_bytes_per_dispatch: {kb:.0f}")
         print(f"copy_rdreq_bytes: {cb:.0f}")
         print(f"rdreq_over_scaled_fetch: {kb / (kf * sf * 1024.0):.4f}")
-    print(f"source_sha256: {source_hash()}")
+    srcs = [os.path.join("mixture_experts_ffn_02_amd/csrc", f) for f in args.sources] if args.sources else GEMM_SOURCES
+    print(f"sources: {' '.join(os.path.basename(f) for f in srcs)}")
+    print(f"source_sha256: {source_hash(srcs)}")
+
+
+def _durations(d: str):
+    """Kernel durations (ns) per dispatch from a counter run's timestamps."""
+    path = _find(d, "counter_collection.csv")
+    out, seen = {}, set()
+    for r in csv.DictReader(open(path)):
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        if key in seen:
+            continue
+        seen.add(key)
+        out.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
 
 
 def mfma(args) -> None:
     """Matrix-core use of every launch of the kernels matching --kernel:
-    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) over GRBM_GUI_ACTIVE
-    (summed over the XCDs, so divided by their count) times the SIMD count,
-    and the bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512 flops)."""
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) over the cycles of the
+    launch (GRBM_GUI_ACTIVE, summed over the XCDs, so divided by their count)
+    times the SIMD count; the clock those cycles imply over the dispatch's
+    duration; and the bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts
+    units of 512 flops)."""
     busy = _counter(args.dir, "SQ_VALU_MFMA_BUSY_CYCLES")
     mops = _counter(args.dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     gui = _counter(args.dir, "GRBM_GUI_ACTIVE")
+    dur = _durations(args.dir)
     print("# matrix-core use from rocprofv3 counters")
     print(f"# command: {args.cmd}")
-    print(f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} * {args.simds}); "
-          f"flops = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16")
-    print(f"{'launches':>8} {'mfma_busy':>9} {'gflop':>10} {'cycles':>12}  kernel")
+    print(f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} * {args.simds}); "
+          f"clock = GRBM_GUI_ACTIVE / {args.xcds} / duration; flops = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16; "
+          f"pf_at_clock = the bf16 MFMA rate the clock allows (2.5 PFLOP/s at 2.4 GHz)")
+    print(f"{'launches':>8} {'mfma_busy':>9} {'clock_ghz':>9} {'pf_at_clock':>11} {'gflop':>10} {'avg_us':>10}  kernel")
     for name in busy:
         if not any(k in name for k in args.kernel):
             continue
         b = statistics.mean(busy[name])
         m = statistics.mean(mops.get(name, [0.0]))
         g = statistics.mean(gui.get(name, [0.0])) / args.xcds
+        us = statistics.mean(dur.get(name, [0])) / 1e3
         util = b / (g * args.simds) if g else 0.0
-        short = name.replace("moe::(anonymous namespace)::", "")[:90]
-        print(f"{len(busy[name]):8d} {util:9.3f} {m * 512 / 1e9:10.1f} {g:12.0f}  {short}")
+        ghz = g / (us * 1e3) if us else 0.0
+        short = name.replace("moe::(anonymous namespace)::", "")[:80]
+        print(f"{len(busy[name]):8d} {util:9.3f} {ghz:9.2f} {2.5 * ghz / 2.4:11.2f} {m * 512 / 1e9:10.1f} {us:10.1f}  {short}")
 
 
 def main(argv=None) -> None:
@@ -175,6 +198,8 @@ def main(argv=None) -> None:
                         "both with and without a data-moving option)")
     b.add_argument("--algorithmic", type=float, default=0.0, help="algorithmic bytes per launch, for the ratio")
     b.add_argument("--note", default="")
+    b.add_argument("--sources", nargs="*", default=None,
+                   help="kernel sources (file names under csrc/) whose hash the summary records (default: the GEMM's)")
     b.add_argument("--cmd", required=True)
     c = sub.add_parser("mfma")
     c.add_argument("dir")
