@@ -27,8 +27,8 @@ struct RouteLaunch {
   double* mpart;          // [n_blocks, E + 1] metric partials (score sums, sum of lse^2), or null
 };
 // Tokens per router block (its rows of the block histograms) for a launch
-// with a logits buffer over T tokens.
-int route_tokens_per_block(int E, int64_t T);
+// with a logits buffer over T tokens of d features.
+int route_tokens_per_block(int E, int64_t T, int d);
 size_t route_lds_bytes(int E, int k);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 // The fp32 logits alone ([T, E] into a.logits), the same fma chains as the router.

@@ -82,7 +82,7 @@ Layout make_layout(const moe_layer* L, int64_t T) {
   const int64_t E = L->n_experts, k = L->top_k, d = L->d_model, f = L->d_ff, fs = L->d_ff_shared;
   const int64_t rows = T * k;
   const int eb = elem_bytes(L->dtype);
-  const int64_t tpb_r = route_tokens_per_block((int)E, T), tpb_h = hist_tokens_per_block();
+  const int64_t tpb_r = route_tokens_per_block((int)E, T, (int)L->d_model), tpb_h = hist_tokens_per_block();
   const int64_t tpb = tpb_r < tpb_h ? tpb_r : tpb_h;
   o.nb = (T + tpb - 1) / tpb;
   const bool merged = shared_as_group(L, T);
@@ -198,7 +198,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   if (merged && T * (int64_t)(k + 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
   const int n_groups = E + (merged ? 1 : 0);
   const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model);
-  const int tpb = route_tokens_per_block(E, T);
+  const int tpb = route_tokens_per_block(E, T, L->d_model);
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
   mark(tm, MOE_PHASE_ROUTE, s);
@@ -756,7 +756,7 @@ moe_status moe_route_ex(const moe_layer* L, const void* x, int64_t T, const moe_
   int32_t* hist = counts_p ? at<int32_t>(ws, lo.hist) : nullptr;
   const RouteLaunch r = route_launch(L, x, T, opts, topk_idx, topk_w, hist, nullptr, ws, lo);
   MOE_TRY(launch_route(r, s));
-  const int tpb = route_tokens_per_block(L->n_experts, T);
+  const int tpb = route_tokens_per_block(L->n_experts, T, L->d_model);
   const int nb = (int)((T + tpb - 1) / tpb);
   if (counts_p) MOE_TRY(launch_counts(hist, nb, L->n_experts, counts_p, s));
   if (metrics) MOE_TRY(launch_router_metrics(r.mpart, nb, counts_p, T, L->n_experts, L->top_k, opts->metrics, s));

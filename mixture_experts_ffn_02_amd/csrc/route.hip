@@ -13,6 +13,8 @@
 //   * logits: one fma chain per (token, expert), features ascending, from +0;
 //   * exp: canonical_exp below (Cody-Waite reduction, Taylor degree 7);
 //   * softmax normaliser: summed over experts in ascending order.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -57,6 +59,24 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N - 1 (unrolled,
+// with every i a compile-time constant).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// acc += (w of lane L of this lane's 16-lane row) * x: v_fmac_f32 with a DPP
+// row_newbcast operand. w must not be written by a VALU instruction right
+// before (the DPP read hazard): here it always comes from a memory load.
+template <int L>
+__device__ __forceinline__ void fmac_bcast(float& acc, float w, float x) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(w), "v"(x), "n"(L));
+}
+
 // Launch shape per padded expert count EP (power of two, 8..1024):
 //   ME experts x MT tokens per thread, EG expert groups x TG token groups
 //   = 256 threads, TT = TG*MT tokens per block, at most KC features per LDS
@@ -93,16 +113,30 @@ ROUTE_SHAPE(1024, 16, 4, 8)
 // there is no gate product to share, so small blocks spread over the chip.
 constexpr int kSelTT = 16;
 
-template <int EP, bool FROM_LOGITS = false>
+// Gate product with the router weights broadcast from registers (up to 32
+// experts, many tokens): a block holds 64 tokens, lane l of each wave owns
+// token l, and wave w the experts w*EP/4 .. (w+1)*EP/4 - 1 (ME = EP/4
+// chains per lane). Token rows are staged in fp32 through LDS (kDppKC
+// features per stage); the router weights go straight from memory into
+// registers, each 16-lane row of a wave holding the wave's ME experts x
+// 16/ME runs of 4 features, and every fma reads its weight from the lane
+// that holds it with a DPP row_share operand (d a multiple of kDppKC). Per fma a lane reads 1 byte of
+// LDS (a token's 4 features serve 4 x ME fmas) where the LDS-staged shapes
+// read 4-8.
+constexpr int kDppTT = 64;
+constexpr int kDppKC = 128;
+constexpr int kDppPitch = kDppKC + 4;  // floats; 16 lanes' rows fall 16 bytes apart in the banks
+
+template <int EP, bool FROM_LOGITS = false, bool DPP = false>
 struct RouteLds {
   using S = RouteShape<EP>;
-  static constexpr int TT = FROM_LOGITS ? kSelTT : S::TT;
+  static constexpr int TT = FROM_LOGITS ? kSelTT : (DPP ? kDppTT : S::TT);
   // One token per thread (MT = 1): stage rows are token- and expert-major,
   // padded by 4 floats, so that a lane reads 4 features with one 16-byte
   // load. Otherwise feature-major ([feature][token] and [feature][expert]).
   static constexpr bool kRows = S::MT == 1;
   static constexpr int kPitch = kRows ? S::KC + 4 : S::KC;
-  static constexpr int kStage = FROM_LOGITS ? 0 : 2 * kPitch * (S::TT + EP);  // floats
+  static constexpr int kStage = FROM_LOGITS ? 0 : (DPP ? 2 * kDppPitch * kDppTT : 2 * kPitch * (S::TT + EP));  // floats
   static constexpr int kLogits = TT * (EP + 1);                               // floats
   static constexpr int kUnion = kStage > kLogits ? kStage : kLogits;
   static constexpr int kWords = (TT + 63) / 64;
@@ -163,10 +197,10 @@ __device__ void block_hist_rank(const int* sel, int tt_count, int k, int E, int 
 
 // FROM_LOGITS: the logits were computed by k_logits into p.logits [T, E];
 // otherwise the gate product runs here, fused with the selection.
-template <int EP, typename XT, bool FROM_LOGITS>
+template <int EP, typename XT, bool FROM_LOGITS, bool DPP = false>
 __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
   using S = RouteShape<EP>;
-  using L = RouteLds<EP, FROM_LOGITS>;
+  using L = RouteLds<EP, FROM_LOGITS, DPP>;
   constexpr int ME = S::ME, MT = S::MT, KC = S::KC, EG = S::EG, TG = S::TG, TT = L::TT;
   // features per register group of the gate-product loop (fewer when a
   // thread holds many chains, to bound the registers)
@@ -199,6 +233,103 @@ __global__ __launch_bounds__(256) void k_route(RouteLaunch p) {
       const int tt = q / EP, e = q % EP;
       lg[tt * (EP + 1) + e] = (tt < tt_count && e < E) ? p.logits[(t0 + tt) * E + e] : 0.0f;
     }
+    __syncthreads();
+  } else if constexpr (DPP) {
+    static_assert(EP >= 8 && EP <= 32, "register-broadcast gate product: 8 to 32 experts");
+    constexpr int MD = EP / 4;         // chains per lane
+    constexpr int QN = 16 / MD;        // 4-feature runs per expert in a 16-lane row
+    constexpr int FC = 4 * QN;         // features per weight chunk
+    constexpr int V = XLoad<XT>::V;
+    const int lane = tid & 63, wave = tid >> 6;
+    constexpr int kc = kDppKC;  // d is a multiple (launch_route_ep checks)
+    const int nstage = d / kc;
+    // weights: lane l loads expert wave*MD + (l%16)/QN, features 4((l%16)%QN) .. +3 of each chunk
+    // (experts past E read expert E-1: their logits are never used)
+    const int we = wave * MD + (lane & 15) / QN, wq = (lane & 15) % QN;
+    const float* wrow = wr + (size_t)(we < E ? we : E - 1) * d + 4 * wq;
+    constexpr int XL = kDppTT * kc / V / 256;  // 16-byte x loads per thread per stage
+    constexpr int xch = kc / V;                // 16-byte loads per token row and stage
+    u32x4 xr[XL];
+    // rows past the batch read its last token (their logits are never used),
+    // so that every load is unconditional
+    auto load_x = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < XL; ++i) {
+        const int q = tid + i * 256, c = q % xch;
+        int tt = q / xch;
+        tt = tt < tt_count ? tt : tt_count - 1;
+        xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * d + s * kc + c * V);
+      }
+    };
+    auto store_x = [&](int buf) {
+      float* xs = uni + buf * kDppPitch * kDppTT;
+#pragma unroll
+      for (int i = 0; i < XL; ++i) {
+        const int q = tid + i * 256, tt = q / xch, c = q % xch;
+        float f[V];
+        XLoad<XT>::widen(xr[i], f);
+#pragma unroll
+        for (int v = 0; v < V; v += 4)
+          *reinterpret_cast<f32x4*>(xs + tt * kDppPitch + c * V + v) = f32x4{f[v], f[v + 1], f[v + 2], f[v + 3]};
+      }
+    };
+    float acc[MD];
+#pragma unroll
+    for (int j = 0; j < MD; ++j) acc[j] = 0.0f;
+    // the weights of a stage, loaded a stage ahead into one of two register
+    // sets (stages unrolled by two, so that the sets are named statically)
+    constexpr int CH = kc / FC;
+    f32x4 wa[CH], wb[CH];
+    auto load_w = [&](f32x4 (&w)[CH], int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) w[c] = *reinterpret_cast<const f32x4*>(wrow + s * kc + c * FC);
+    };
+    // features s*kc + c*FC + 4q + r, ascending: run q of every expert sits
+    // in lane e*QN + q of the lane's 16-lane row. One v_fmac_f32 per
+    // (expert, feature), its weight broadcast by DPP from that lane (the
+    // compiler does not fold a DPP move into fmac itself).
+    auto compute = [&](const f32x4 (&w)[CH], int s) __attribute__((always_inline)) {
+      const float* xrow = uni + (s & 1) * kDppPitch * kDppTT + lane * kDppPitch;
+      static_for<CH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        static_for<QN>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const f32x4 xv = *reinterpret_cast<const f32x4*>(xrow + c * FC + 4 * q);
+          static_for<4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            static_for<MD>([&](auto ec) {
+              constexpr int e = decltype(ec)::value;
+              fmac_bcast<e * QN + q>(acc[e], w[c][r], xv[r]);
+            });
+          });
+        });
+      });
+    };
+    load_x(0);
+    load_w(wa, 0);
+    store_x(0);
+    __syncthreads();
+    // The next stage's loads are unconditional (the last stage loads itself
+    // again, into the buffer no one reads): a guarded load makes the
+    // compiler's wait for the current weights count only the loads on the
+    // path without it, which waits for the prefetch too.
+    for (int s = 0; s < nstage; s += 2) {
+      const int s1 = s + 1 < nstage ? s + 1 : s;
+      load_x(s1);
+      load_w(wb, s1);
+      compute(wa, s);
+      store_x((s + 1) & 1);
+      __syncthreads();
+      if (s + 1 >= nstage) break;
+      const int s2 = s + 2 < nstage ? s + 2 : s + 1;
+      load_x(s2);
+      load_w(wa, s2);
+      compute(wb, s + 1);
+      store_x(s & 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < MD; ++j) lg[lane * (EP + 1) + wave * MD + j] = acc[j];
     __syncthreads();
   } else {
   // ---- gate product: logits[tt][e] = fma chain over features ascending
@@ -855,9 +986,27 @@ bool route_split_ep(int E, int64_t T) {
   return E >= 64 && nb < per_cu * (int64_t)cu_count();
 }
 
+// The register-broadcast gate product: up to 32 experts and enough tokens
+// for two 64-token blocks per CU.
+#ifndef MOE_DPP_MIN_BLOCKS_PER_CU
+#define MOE_DPP_MIN_BLOCKS_PER_CU 2
+#endif
+template <int EP>
+bool route_dpp_ep(int64_t T, int d) {
+  return EP <= 32 && d % kDppKC == 0 && (T + kDppTT - 1) / kDppTT >= (int64_t)MOE_DPP_MIN_BLOCKS_PER_CU * cu_count();
+}
+
 template <int EP>
 hipError_t launch_route_ep(const RouteLaunch& a, hipStream_t s) {
   using S = RouteShape<EP>;
+  if constexpr (EP <= 32) {
+    if (route_dpp_ep<EP>(a.T, a.d)) {
+      const size_t lds_d = RouteLds<EP, false, true>::bytes(a.k);
+      const dim3 g((unsigned)((a.T + kDppTT - 1) / kDppTT));
+      return a.dtype == 1 ? launch_k(k_route<EP, uint16_t, false, true>, g, lds_d, s, a)
+                          : launch_k(k_route<EP, float, false, true>, g, lds_d, s, a);
+    }
+  }
   const size_t lds = RouteLds<EP>::bytes(a.k);
   const int64_t nb = (a.T + S::TT - 1) / S::TT;
   const size_t lds_sel = RouteLds<EP, true>::bytes(a.k);
@@ -882,11 +1031,11 @@ int padded_experts(int E) {
 
 }  // namespace
 
-int route_tokens_per_block(int E, int64_t T) {
+int route_tokens_per_block(int E, int64_t T, int d) {
   switch (padded_experts(E)) {
-    case 8: return route_split_ep<8>(E, T) ? kSelTT : RouteShape<8>::TT;
-    case 16: return route_split_ep<16>(E, T) ? kSelTT : RouteShape<16>::TT;
-    case 32: return route_split_ep<32>(E, T) ? kSelTT : RouteShape<32>::TT;
+    case 8: return route_dpp_ep<8>(T, d) ? kDppTT : RouteShape<8>::TT;
+    case 16: return route_dpp_ep<16>(T, d) ? kDppTT : RouteShape<16>::TT;
+    case 32: return route_dpp_ep<32>(T, d) ? kDppTT : RouteShape<32>::TT;
     case 64: return route_split_ep<64>(E, T) ? kSelTT : RouteShape<64>::TT;
     case 128: return route_split_ep<128>(E, T) ? kSelTT : RouteShape<128>::TT;
     case 256: return route_split_ep<256>(E, T) ? kSelTT : RouteShape<256>::TT;

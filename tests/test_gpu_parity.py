@@ -1,7 +1,7 @@
 """The HIP path against the CPU oracle through the C ABI, on seeded layers
 small enough for the oracle to finish in seconds yet spanning several tiles
 of every kernel and a ragged tail: expert ids, counts and dispatch order
-bit-exact, combine weights within 1e-6 relative, outputs within
+bit-exact, combine weights bit-exact, outputs within
 1e-5 RMS(y) (fp32) or 2e-2 RMS(y) (bf16)."""
 import numpy as np
 import pytest
@@ -58,6 +58,14 @@ CASES = [
     # 4 x 4 (fp32 tokens)
     C("split_mid_ring", T=4100, d_model=256, n_experts=256, top_k=8, d_ff=64),
     C("split_wide_f32", T=8200, d_model=192, n_experts=256, top_k=4, d_ff=64, dtype="f32", bias_range=0.05),
+    # the register-broadcast router (up to 32 experts, at least two 64-token
+    # blocks per CU of a 256-CU part): 16 experts with 128-feature stages over
+    # an odd number of stages, 6 of 8 padded experts in fp32 with a ragged
+    # last block, and 20 of 32 over two stages
+    C("bcast_router_e16", T=32768, d_model=384, n_experts=16, top_k=4, d_ff=64, bias_range=0.1),
+    C("bcast_router_e6_f32", T=33000, d_model=128, n_experts=6, top_k=2, d_ff=64, dtype="f32", score="sigmoid",
+      bias_range=0.2),
+    C("bcast_router_e20", T=32790, d_model=256, n_experts=20, top_k=3, d_ff=64, score="sigmoid", zipf_s=1.1),
 ]
 
 # Wide-expert layers whose grouped GEMMs run the tile shapes of the large

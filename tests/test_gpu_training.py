@@ -41,6 +41,10 @@ CASES = [
       bias_range=0.2, bias_on_logits=True),
     # no bias at all: noise alone in logit space
     C("noise_only_e32", T=1030, d_model=64, n_experts=32, top_k=4, d_ff=64, score="sigmoid", zipf_s=1.0),
+    # the register-broadcast router (16 experts, 32768 tokens): logit-space
+    # bias, noise and the metric partials of 64-token blocks
+    C("logit_bias_e16_bcast", T=32768, d_model=256, n_experts=16, top_k=2, d_ff=64, score="softmax",
+      bias_range=0.3, bias_on_logits=True),
 ]
 
 
