@@ -58,6 +58,9 @@ CASES = [
     # 4 x 4 (fp32 tokens)
     C("split_mid_ring", T=4100, d_model=256, n_experts=256, top_k=8, d_ff=64),
     C("split_wide_f32", T=8200, d_model=192, n_experts=256, top_k=4, d_ff=64, dtype="f32", bias_range=0.05),
+    # split path with 4 x 4 chains per thread on 64 x 64 blocks in bf16: 96
+    # experts (the second expert block half empty), a ragged last token block
+    C("split_wide_e96", T=16400, d_model=192, n_experts=96, top_k=6, d_ff=64, score="sigmoid", bias_range=0.1),
     # the register-broadcast router (up to 32 experts, at least two 64-token
     # blocks per CU of a 256-CU part): 16 experts with 128-feature stages over
     # an odd number of stages, 6 of 8 padded experts in fp32 with a ragged
