@@ -259,8 +259,8 @@ def cold_phases(layer, x, y, steps: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the layer's data-parallel shards are independent, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's data-parallel "
+              f"shards run independently, one per GPU, and exchange nothing in the forward pass)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
