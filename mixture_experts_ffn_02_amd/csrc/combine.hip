@@ -18,50 +18,51 @@ template <int KG>
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const float* __restrict__ y_perm,
                                                  const int32_t* __restrict__ row_of, const float* __restrict__ w,
                                                  const float* __restrict__ y_shared, float* __restrict__ y) {
-  __shared__ int rows_s[4][32];
-  __shared__ float w_s[4][32];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the token is wave-uniform: its row ids and weights are read with scalar
+  // loads, and every slot test below is a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  const bool valid = t < T;
-  if (valid && lane < k) {
-    rows_s[wave][lane] = row_of[t * k + lane];
-    w_s[wave][lane] = w[t * k + lane];
-  }
-  __syncthreads();
-  if (!valid) return;
+  if (t >= T) return;
   const int n4 = d >> 2;
   const int span = (n4 + gridDim.y - 1) / gridDim.y;  // float4 columns of this block
   const int c0 = blockIdx.y * span, c1 = c0 + span < n4 ? c0 + span : n4;
   const int64_t n_rows = T * k;
   const f32x4* Y = reinterpret_cast<const f32x4*>(y_perm);
-  for (int c = c0 + lane; c < c1; c += 64) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    // slots in groups of KG: the group's loads are issued together (a slot
-    // past k or an invalid row id reads row 0 and contributes nothing), then
-    // added in slot order
-    for (int j0 = 0; j0 < k; j0 += KG) {
+  for (int j0 = 0; j0 < k; j0 += KG) {
+    // slots j0 .. j0 + KG - 1: base of each row (a slot past k or an invalid
+    // row id reads row 0 and contributes nothing)
+    const f32x4* src[KG];
+    float wj[KG];
+    bool use[KG];
+#pragma unroll
+    for (int q = 0; q < KG; ++q) {
+      const int j = j0 + q < k ? j0 + q : k - 1;  // every load in range
+      const int r = __builtin_amdgcn_readfirstlane(row_of[t * k + j]);
+      use[q] = j0 + q < k && r >= 0 && r < n_rows;
+      wj[q] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, w[t * k + j])));
+      src[q] = Y + (size_t)(use[q] ? r : 0) * n4;
+    }
+    for (int c = c0 + lane; c < c1; c += 64) {
+      float* out = y + ((size_t)t * n4 + c) * 4;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j0 > 0) acc = *reinterpret_cast<const f32x4*>(out);  // the earlier slot groups' sum
       f32x4 v[KG];
 #pragma unroll
-      for (int q = 0; q < KG; ++q) {
-        const int r = j0 + q < k ? rows_s[wave][j0 + q] : -1;
-        const int rr = (r >= 0 && r < n_rows) ? r : 0;
-        v[q] = __builtin_nontemporal_load(&Y[(size_t)rr * n4 + c]);  // read once: streaming
-      }
+      for (int q = 0; q < KG; ++q) v[q] = __builtin_nontemporal_load(src[q] + c);  // read once: streaming
 #pragma unroll
       for (int q = 0; q < KG; ++q) {
-        const int r = j0 + q < k ? rows_s[wave][j0 + q] : -1;
-        if (r < 0 || r >= n_rows) continue;  // invalid row ids contribute nothing
-        const float wj = w_s[wave][j0 + q];
+        if (!use[q]) continue;  // invalid row ids contribute nothing
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wj, v[q][e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wj[q], v[q][e], acc[e]);
       }
-    }
-    if (y_shared) {
-      const f32x4 sv = reinterpret_cast<const f32x4*>(y_shared)[(size_t)t * n4 + c];
+      if (y_shared && j0 + KG >= k) {
+        const f32x4 sv = reinterpret_cast<const f32x4*>(y_shared)[(size_t)t * n4 + c];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += sv[q];
+        for (int q = 0; q < 4; ++q) acc[q] += sv[q];
+      }
+      *reinterpret_cast<f32x4*>(out) = acc;
     }
-    reinterpret_cast<f32x4*>(y)[(size_t)t * n4 + c] = acc;
   }
 }
 
