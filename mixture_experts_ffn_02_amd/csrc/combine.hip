@@ -3,9 +3,11 @@
 // one weighted sum).
 //   y[t] = sum_{j<k} w[t,j] * Y[row_of[t,j]]  (+ S[t], weight 1, added last)
 // A gather: one wave per token reads its k expert rows and writes its output
-// row once, in fp32, slots in order (each lane keeps up to eight row loads in
-// flight). No atomics, so the result is the same
-// bits on every run. When the tokens are too few to give every CU work, the
+// row in fp32, slots in order, each lane keeping a group of up to eight row
+// loads in flight (with more than eight slots the row is written after each
+// group and read back for the next, which leaves every sum unchanged). The
+// token's row ids and weights are wave-uniform. No atomics, so the result is
+// the same bits on every run. When the tokens are too few to give every CU work, the
 // row is also split into column ranges over grid.y (each element's sum is
 // unchanged).
 #include "common.h"
