@@ -41,11 +41,16 @@
 //     spans the tile's rows, whose range check drops the rows past the
 //     tile's end), so no LDS is needed between tiles and the matrix cores
 //     never wait for a new tile's first stage.
-//   * Copies use global_load_lds_dwordx4 (lane i of a wave writes bytes
+//   * Copies use buffer_load_dwordx4 ... lds (lane i of a wave writes bytes
 //     16i..16i+15 of a 1 KB run of LDS rows); the 16-byte chunks of an LDS
 //     row are XOR-swizzled (applied on the global side) so that the
 //     fragment reads of 16 consecutive rows hit distinct banks (measured: no
-//     bank conflicts).
+//     bank conflicts). Buffer rather than global (FLAT) copies: while a FLAT
+//     copy into LDS is in flight the compiler cannot order LDS reads in the
+//     lgkm counter, and so made every fragment wait lgkmcnt(0); with buffer
+//     copies each MFMA waits for its own two fragments only (reads issued
+//     weights first), and the resource's range check bounds every copy.
+//     Measured 2-4% off the down launches, gate/up unchanged.
 //   * Persistent grid, one block per CU, tiles split into 8 contiguous
 //     ranges, one per XCD (block b runs on XCD b % 8, measured), each walked
 //     in raster groups of GM row tiles x all column tiles so the blocks
@@ -71,6 +76,17 @@ constexpr int kNH = 5;                // half-stage buffers
 // the copies to the second wave of each SIMD alone was 6% slower).
 constexpr int kRuns = kHalf / 1024 / 8;  // 1 KB copies per wave per half-stage (4)
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Word 3 of a raw buffer resource (32-bit data format; offsets in bytes,
+// range-checked against the resource's size).
+constexpr uint32_t kRsrcWord3 = 0x00020000;
+// A block-uniform pointer, said to be so: a buffer resource built from a
+// value the compiler holds in vector registers becomes a loop over lanes.
+__device__ __forceinline__ const unsigned char* uni(const unsigned char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  return reinterpret_cast<const unsigned char*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                                                (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v));
+}
 
 // XOR key of LDS row `row` (128-byte rows, 8 chunks): the 16 lanes of one
 // ds_read_b128 phase read one logical chunk of 16 consecutive rows; rows r
@@ -194,26 +210,39 @@ void k_gemm8(GemmLaunch g) {
       }
     return false;
   };
-  // Per tile, for the copies: the source row of each of this lane's A runs
-  // (run 8 i + wave covers tile rows 64 i + 8 wave .. +7; rows past the
-  // tile's end read a valid row whose results are never stored) and the
-  // weight bases (gate/up: runs with i >= 2 are up rows).
+  // Per tile, for the copies (buffer loads: a scalar base and size, 32-bit
+  // lane offsets): the byte offset of this lane's source row of each of its
+  // A runs from abase (run 8 i + wave covers tile rows 64 i + 8 wave .. +7;
+  // rows past the tile's end read a valid row whose results are never
+  // stored) and the weight bases (gate/up: runs with i >= 2 are up rows).
+  // Gathered rows are offsets into all of A (under 4 GiB, which the launch
+  // checks), contiguous ones into the tile's own rows.
   struct Src {
-    int32_t a_row[kRuns];
+    uint32_t a_off[kRuns];
+    const unsigned char* abase;
+    uint32_t a_bytes;
     const unsigned char* b0;
     const unsigned char* b1;
   };
+  const unsigned char* const A = reinterpret_cast<const unsigned char*>(g.a);
   auto make_src = [&](const Tile8& t, Src& sr) __attribute__((always_inline)) {
+    if (g.a_rows) {
+      sr.abase = A;
+      sr.a_bytes = (uint32_t)(g.a_row_count * (int64_t)kbytes);
+    } else {
+      sr.abase = A + (size_t)t.row0 * kbytes;
+      sr.a_bytes = (uint32_t)((int64_t)t.rows * kbytes);
+    }
 #pragma unroll
     for (int i = 0; i < kRuns; ++i) {
       int r = 8 * (kSlots * i + wave) + lrow;
       r = r < t.rows ? r : t.rows - 1;
-      int64_t src = t.row0 + r;
+      int64_t src = r;
       if (g.a_rows) {
-        src = g.a_rows[src];
+        src = g.a_rows[t.row0 + r];
         src = src < 0 ? 0 : (src >= g.a_row_count ? g.a_row_count - 1 : src);
       }
-      sr.a_row[i] = (int32_t)src;
+      sr.a_off[i] = (uint32_t)src * (uint32_t)kbytes + lchunk * 16;
     }
     // block-uniform bases; the lane offset b_lane is added at the copy
     const bool xg = t.e == g.extra_group;
@@ -225,27 +254,37 @@ void k_gemm8(GemmLaunch g) {
                          (size_t)t.n0 * kbytes
                    : sr.b0;
   };
-  const unsigned char* const A = reinterpret_cast<const unsigned char*>(g.a);
+  const uint32_t w_bytes = (uint32_t)((GATEUP ? kBR / 2 : kBR) * kbytes);  // weight rows of one operand of a tile
   // Copy runs I0 .. I0 + NR - 1 of half-stage h of the tile described by sr
   // (even h: weight rows of stage h / 2, odd: A rows) into ring buffer `buf`.
   auto issue_runs = [&](const Src& sr, int h, int buf, auto i0c, auto nc) __attribute__((always_inline)) {
     constexpr int I0 = decltype(i0c)::value, NR = decltype(nc)::value;
     unsigned char* dst = lds + buf * kHalf + wave * 1024;
-    const size_t koff = (size_t)(h >> 1) * kSB;
+    const uint32_t koff = (uint32_t)(h >> 1) * kSB;
     if ((h & 1) == 1) {
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)uni(sr.abase), 0, (uint32_t)__builtin_amdgcn_readfirstlane((int)sr.a_bytes), kRsrcWord3);
 #pragma unroll
-      for (int i = I0; i < I0 + NR; ++i)
-        lds_dma16(A + (size_t)(uint32_t)sr.a_row[i] * kbytes + koff + lchunk * 16, dst + i * kSlots * 1024);
+      for (int i = I0; i < I0 + NR; ++i) {
+        const uint32_t vo = sr.a_off[i];  // (a local: passing the array element disables the kernel's host stub)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024),
+                                                 16, vo, koff, 0, 0);
+      }
       return;
     }
     // weight run i starts at weight row 8 kSlots i (gate/up: the second half
     // of the runs are up rows)
+    const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void*)uni(sr.b0), 0, w_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc((void*)uni(sr.b1), 0, w_bytes, kRsrcWord3);
 #pragma unroll
     for (int i = I0; i < I0 + NR; ++i) {
-      const unsigned char* src = (GATEUP && i >= kRuns / 2)
-                                     ? sr.b1 + (size_t)(8 * kSlots * (i - kRuns / 2)) * kbytes + koff + b_lane
-                                     : sr.b0 + (size_t)(8 * kSlots * i) * kbytes + koff + b_lane;
-      lds_dma16<STREAM>(src, dst + i * kSlots * 1024);
+      const bool up = GATEUP && i >= kRuns / 2;
+      const uint32_t row = (uint32_t)(8 * kSlots * (up ? i - kRuns / 2 : i)) * (uint32_t)kbytes;
+      __attribute__((address_space(3))) void* d = (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024);
+      if (up)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, d, 16, b_lane, koff + row, 0, STREAM ? 2 : 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, d, 16, b_lane, koff + row, 0, STREAM ? 2 : 0);
     }
   };
   using R0 = std::integral_constant<int, 0>;
@@ -275,10 +314,10 @@ void k_gemm8(GemmLaunch g) {
   auto load_frag = [&](Frag& f, int abuf, int bbuf, int s4) __attribute__((always_inline)) {
     const unsigned char* ab = lds + abuf * kHalf + wm * 128 * kSB + loff[s4];
     const unsigned char* bb = lds + bbuf * kHalf + wrow0 * kSB + loff[s4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const u32x4*>(ab + i * 32 * kSB);
     f.b[0] = *reinterpret_cast<const u32x4*>(bb);
     f.b[1] = *reinterpret_cast<const u32x4*>(bb + kWStep);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const u32x4*>(ab + i * 32 * kSB);
   };
   auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -299,7 +338,7 @@ void k_gemm8(GemmLaunch g) {
   auto epilogue = [&](const Tile8& t) __attribute__((always_inline)) {
     constexpr int EB = GATEUP ? 2 : 4;
     unsigned char* const obase = reinterpret_cast<unsigned char*>(g.out) + (size_t)t.row0 * g.N * EB;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, t.rows * g.N * EB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, t.rows * g.N * EB, kRsrcWord3);
     const int col = (GATEUP ? t.n0 + wn * 32 : t.n0 + wn * 64) + (lane & 31);
     const int lane_off = ((wm * 128 + 4 * (lane >> 5)) * g.N + col) * EB;
 #pragma unroll
@@ -435,10 +474,16 @@ void k_gemm8(GemmLaunch g) {
 
 }  // namespace
 
+// The copies address gathered rows by 32-bit offsets into all of A.
+static bool gather_fits(const GemmLaunch& g) {
+  return !g.a_rows || g.a_row_count * 2 * (int64_t)g.K < ((int64_t)1 << 32);
+}
+
 // 256 x 256 eight-wave tiles for bf16 forward products; the caller checks
-// dtype, K % 64 and N (gate/up: % 128, down: % 256).
+// dtype, K % 64, N (gate/up: % 128, down: % 256) and a gathered A under 4 GiB.
 hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
-  if (g.dtype != 1 || g.K % kKE || g.K < 3 * kKE || (g.gateup ? g.N % 128 : g.N % 256) || g.bt || g.koffs || g.out_g)
+  if (g.dtype != 1 || g.K % kKE || g.K < 3 * kKE || (g.gateup ? g.N % 128 : g.N % 256) || g.bt || g.koffs || g.out_g ||
+      !gather_fits(g))
     return hipErrorInvalidValue;
   int64_t blocks = cu_count();
   blocks = (blocks + kXcd - 1) / kXcd * kXcd;
@@ -475,7 +520,7 @@ hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
 bool gemm8_fits(const GemmLaunch& g, int bm) {
   return MOE_GEMM8 && bm == 256 && g.dtype == 1 && g.K % kKE == 0 && g.K >= 3 * kKE &&
          (g.gateup ? g.N % 128 == 0 : g.N % 256 == 0) &&
-         !g.bt && !g.koffs && !g.out_g;
+         !g.bt && !g.koffs && !g.out_g && gather_fits(g);
 }
 
 hipError_t launch_gemm_fwd(const GemmLaunch& g, int bm, hipStream_t s) {
