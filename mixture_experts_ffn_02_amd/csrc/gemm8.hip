@@ -41,16 +41,18 @@
 //     spans the tile's rows, whose range check drops the rows past the
 //     tile's end), so no LDS is needed between tiles and the matrix cores
 //     never wait for a new tile's first stage.
-//   * Copies use buffer_load_dwordx4 ... lds (lane i of a wave writes bytes
-//     16i..16i+15 of a 1 KB run of LDS rows); the 16-byte chunks of an LDS
-//     row are XOR-swizzled (applied on the global side) so that the
-//     fragment reads of 16 consecutive rows hit distinct banks (measured: no
-//     bank conflicts). Buffer rather than global (FLAT) copies: while a FLAT
-//     copy into LDS is in flight the compiler cannot order LDS reads in the
-//     lgkm counter, and so made every fragment wait lgkmcnt(0); with buffer
-//     copies each MFMA waits for its own two fragments only (reads issued
-//     weights first), and the resource's range check bounds every copy.
-//     Measured 2-4% off the down launches, gate/up unchanged.
+//   * Copies write 1 KB runs of LDS rows (lane i of a wave writes bytes
+//     16i..16i+15); the 16-byte chunks of an LDS row are XOR-swizzled
+//     (applied on the global side) so that the fragment reads of 16
+//     consecutive rows hit distinct banks (measured: no bank conflicts).
+//     Down products copy with buffer_load_dwordx4 ... lds, gate/up with
+//     global_load_lds_dwordx4. While a global (FLAT) copy into LDS is in
+//     flight the compiler cannot order LDS reads in the lgkm counter and
+//     makes every fragment wait lgkmcnt(0); with buffer copies each MFMA
+//     waits for its own two fragments only (reads issued weights first),
+//     which took 2-4% off the down launches. For gate/up the buffer copies
+//     were no faster and fetched about 50% more bytes past L2 (105 vs 70 GB
+//     per launch at the DeepSeek-style layer), so those stay global.
 //   * Persistent grid, one block per CU, tiles split into 8 contiguous
 //     ranges, one per XCD (block b runs on XCD b % 8, measured), each walked
 //     in raster groups of GM row tiles x all column tiles so the blocks
@@ -210,13 +212,14 @@ void k_gemm8(GemmLaunch g) {
       }
     return false;
   };
-  // Per tile, for the copies (buffer loads: a scalar base and size, 32-bit
-  // lane offsets): the byte offset of this lane's source row of each of its
-  // A runs from abase (run 8 i + wave covers tile rows 64 i + 8 wave .. +7;
-  // rows past the tile's end read a valid row whose results are never
-  // stored) and the weight bases (gate/up: runs with i >= 2 are up rows).
-  // Gathered rows are offsets into all of A (under 4 GiB, which the launch
-  // checks), contiguous ones into the tile's own rows.
+  // Per tile, for the copies (block-uniform bases and size, 32-bit lane
+  // offsets; down builds buffer resources from them): the byte offset from
+  // abase of this lane's source row of each of its A runs (run 8 i + wave
+  // covers tile rows 64 i + 8 wave .. +7; rows past the tile's end read a
+  // valid row whose results are never stored) and the weight bases
+  // (gate/up: runs with i >= 2 are up rows). Gathered rows are offsets into
+  // all of A (under 4 GiB, which the launch checks), contiguous ones into
+  // the tile's own rows.
   struct Src {
     uint32_t a_off[kRuns];
     const unsigned char* abase;
@@ -254,37 +257,49 @@ void k_gemm8(GemmLaunch g) {
                          (size_t)t.n0 * kbytes
                    : sr.b0;
   };
-  const uint32_t w_bytes = (uint32_t)((GATEUP ? kBR / 2 : kBR) * kbytes);  // weight rows of one operand of a tile
+  const uint32_t w_bytes = (uint32_t)(kBR * kbytes);  // a down tile's weight rows
   // Copy runs I0 .. I0 + NR - 1 of half-stage h of the tile described by sr
   // (even h: weight rows of stage h / 2, odd: A rows) into ring buffer `buf`.
   auto issue_runs = [&](const Src& sr, int h, int buf, auto i0c, auto nc) __attribute__((always_inline)) {
     constexpr int I0 = decltype(i0c)::value, NR = decltype(nc)::value;
     unsigned char* dst = lds + buf * kHalf + wave * 1024;
     const uint32_t koff = (uint32_t)(h >> 1) * kSB;
+    if constexpr (GATEUP) {  // global copies (gate/up: buffer copies fetched 50% more past L2)
+      if ((h & 1) == 1) {
+#pragma unroll
+        for (int i = I0; i < I0 + NR; ++i) lds_dma16(sr.abase + sr.a_off[i] + koff, dst + i * kSlots * 1024);
+        return;
+      }
+      // weight run i starts at weight row 8 kSlots i; the second half of
+      // the runs are up rows
+#pragma unroll
+      for (int i = I0; i < I0 + NR; ++i) {
+        const unsigned char* src = i >= kRuns / 2
+                                       ? sr.b1 + (size_t)(8 * kSlots * (i - kRuns / 2)) * kbytes + koff + b_lane
+                                       : sr.b0 + (size_t)(8 * kSlots * i) * kbytes + koff + b_lane;
+        lds_dma16<STREAM>(src, dst + i * kSlots * 1024);
+      }
+      return;
+    }
+    // down: buffer copies
     if ((h & 1) == 1) {
       const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
           (void*)uni(sr.abase), 0, (uint32_t)__builtin_amdgcn_readfirstlane((int)sr.a_bytes), kRsrcWord3);
 #pragma unroll
       for (int i = I0; i < I0 + NR; ++i) {
-        const uint32_t vo = sr.a_off[i];  // (a local: passing the array element disables the kernel's host stub)
+        const uint32_t vo = sr.a_off[i];  // (a local: passing the array element drops the kernel's host stub)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024),
                                                  16, vo, koff, 0, 0);
       }
       return;
     }
-    // weight run i starts at weight row 8 kSlots i (gate/up: the second half
-    // of the runs are up rows)
-    const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void*)uni(sr.b0), 0, w_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc((void*)uni(sr.b1), 0, w_bytes, kRsrcWord3);
+    // weight run i starts at weight row 8 kSlots i
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)uni(sr.b0), 0, w_bytes, kRsrcWord3);
 #pragma unroll
     for (int i = I0; i < I0 + NR; ++i) {
-      const bool up = GATEUP && i >= kRuns / 2;
-      const uint32_t row = (uint32_t)(8 * kSlots * (up ? i - kRuns / 2 : i)) * (uint32_t)kbytes;
-      __attribute__((address_space(3))) void* d = (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024);
-      if (up)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, d, 16, b_lane, koff + row, 0, STREAM ? 2 : 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, d, 16, b_lane, koff + row, 0, STREAM ? 2 : 0);
+      const uint32_t row = (uint32_t)(8 * kSlots * i) * (uint32_t)kbytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024),
+                                               16, b_lane, koff + row, 0, STREAM ? 2 : 0);
     }
   };
   using R0 = std::integral_constant<int, 0>;
