@@ -212,16 +212,14 @@ void k_gemm8(GemmLaunch g) {
       }
     return false;
   };
-  // Per tile, for the copies (block-uniform bases and size, 32-bit lane
-  // offsets; down builds buffer resources from them): the byte offset from
-  // abase of this lane's source row of each of its A runs (run 8 i + wave
-  // covers tile rows 64 i + 8 wave .. +7; rows past the tile's end read a
-  // valid row whose results are never stored) and the weight bases
-  // (gate/up: runs with i >= 2 are up rows). Gathered rows are offsets into
-  // all of A (under 4 GiB, which the launch checks), contiguous ones into
-  // the tile's own rows.
+  // Per tile, for the copies (block-uniform bases and size; down builds
+  // buffer resources from them): the row of abase that each of this lane's
+  // A runs reads (run 8 i + wave covers tile rows 64 i + 8 wave .. +7; rows
+  // past the tile's end read a valid row whose results are never stored)
+  // and the weight bases (gate/up: runs with i >= 2 are up rows). Gathered
+  // rows index all of A, contiguous ones the tile's own rows.
   struct Src {
-    uint32_t a_off[kRuns];
+    uint32_t a_row[kRuns];
     const unsigned char* abase;
     uint32_t a_bytes;
     const unsigned char* b0;
@@ -245,7 +243,7 @@ void k_gemm8(GemmLaunch g) {
         src = g.a_rows[t.row0 + r];
         src = src < 0 ? 0 : (src >= g.a_row_count ? g.a_row_count - 1 : src);
       }
-      sr.a_off[i] = (uint32_t)src * (uint32_t)kbytes + lchunk * 16;
+      sr.a_row[i] = (uint32_t)src;
     }
     // block-uniform bases; the lane offset b_lane is added at the copy
     const bool xg = t.e == g.extra_group;
@@ -267,7 +265,8 @@ void k_gemm8(GemmLaunch g) {
     if constexpr (GATEUP) {  // global copies (gate/up: buffer copies fetched 50% more past L2)
       if ((h & 1) == 1) {
 #pragma unroll
-        for (int i = I0; i < I0 + NR; ++i) lds_dma16(sr.abase + sr.a_off[i] + koff, dst + i * kSlots * 1024);
+        for (int i = I0; i < I0 + NR; ++i)
+          lds_dma16(sr.abase + (size_t)sr.a_row[i] * kbytes + koff + lchunk * 16, dst + i * kSlots * 1024);
         return;
       }
       // weight run i starts at weight row 8 kSlots i; the second half of
@@ -281,13 +280,15 @@ void k_gemm8(GemmLaunch g) {
       }
       return;
     }
-    // down: buffer copies
+    // down: buffer copies (32-bit offsets: a gathered A under 4 GiB, which
+    // the launch checks)
     if ((h & 1) == 1) {
       const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
           (void*)uni(sr.abase), 0, (uint32_t)__builtin_amdgcn_readfirstlane((int)sr.a_bytes), kRsrcWord3);
 #pragma unroll
       for (int i = I0; i < I0 + NR; ++i) {
-        const uint32_t vo = sr.a_off[i];  // (a local: passing the array element drops the kernel's host stub)
+        // (a local: passing the array element drops the kernel's host stub)
+        const uint32_t vo = sr.a_row[i] * (uint32_t)kbytes + lchunk * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + i * kSlots * 1024),
                                                  16, vo, koff, 0, 0);
       }
@@ -489,13 +490,15 @@ void k_gemm8(GemmLaunch g) {
 
 }  // namespace
 
-// The copies address gathered rows by 32-bit offsets into all of A.
+// The down product's buffer copies address gathered rows by 32-bit offsets
+// into all of A (the forward's down products read their rows in place).
 static bool gather_fits(const GemmLaunch& g) {
-  return !g.a_rows || g.a_row_count * 2 * (int64_t)g.K < ((int64_t)1 << 32);
+  return g.gateup || !g.a_rows || g.a_row_count * 2 * (int64_t)g.K < ((int64_t)1 << 32);
 }
 
 // 256 x 256 eight-wave tiles for bf16 forward products; the caller checks
-// dtype, K % 64, N (gate/up: % 128, down: % 256) and a gathered A under 4 GiB.
+// dtype, K % 64, N (gate/up: % 128, down: % 256) and, for down, a gathered A
+// under 4 GiB.
 hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
   if (g.dtype != 1 || g.K % kKE || g.K < 3 * kKE || (g.gateup ? g.N % 128 : g.N % 256) || g.bt || g.koffs || g.out_g ||
       !gather_fits(g))

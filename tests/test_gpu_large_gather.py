@@ -1,11 +1,10 @@
-"""A layer whose token matrix x holds 2^31 bf16 elements (4 GiB): the eight-wave
-GEMM addresses gathered token rows by 32-bit byte offsets, so its gate/up
-launch hands such an operand to the four-wave kernel, while the down launch
-(expert rows read in place) stays on the eight-wave kernel. Every index of
-2^31 elements and more must be 64-bit on the way. Routing (bit-exact ids and
-combine weights) and outputs (the bf16-activation envelope) of a sample of
-512 tokens, the ragged tail among them, against the oracle, which computes
-them one by one."""
+"""A layer whose token matrix x holds 2^31 bf16 elements (4 GiB), past the reach
+of 32-bit element or byte offsets: the router, the gate/up launch gathering
+token rows (64-bit addresses) and the combine must index it in 64 bits; the
+down launch reads its expert rows in place through buffer resources of one
+tile each. Routing (bit-exact ids and combine weights) and outputs (the
+bf16-activation envelope) of a sample of 512 tokens, the ragged tail among
+them, against the oracle, which computes them one by one."""
 import gc
 
 import numpy as np
