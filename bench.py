@@ -47,6 +47,9 @@ def parse():
                     help="also run one plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--cold-steps", type=int, default=10, help="steps timed with cold caches (0: none)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul (the vendor GEMM library) on dense products of the routed GEMMs' "
+                         "sizes, as a reference")
     return ap.parse_args()
 
 
@@ -173,6 +176,41 @@ def measure_permute(cfg, layer, x, reps: int):
     gbs = by / (ms * 1e-3) / 1e9
     return {"ms": round(ms, 4), "bytes": by, "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
             "note": "moe_permute writing x_perm (not part of moe_forward, whose GEMM gathers the rows)"}
+
+
+def measure_library_gemm(cfg, reps: int):
+    """Reference, not part of the layer: torch.matmul (the vendor GEMM library
+    behind it) on dense products with the routed expert GEMMs' sizes,
+    [T*k, d] x [d, 2 d_ff] (gate and up as one product) and [T*k, d_ff] x
+    [d_ff, d] (down), both operands contiguous, output in the operand dtype.
+    One weight for all rows: no gather, no groups, no SwiGLU, no fp32 output,
+    so it bounds what a plain product of that size reaches on this chip."""
+    import torch
+
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    rows = cfg.T * cfg.top_k
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    peak = PEAK_TFLOPS[cfg.dtype]
+    out = {"note": "torch.matmul on dense operands of the routed GEMMs' sizes (reference only)"}
+    for name, (m, kk, n) in {"gateup_equiv": (rows, cfg.d_model, 2 * cfg.d_ff),
+                             "down_equiv": (rows, cfg.d_ff, cfg.d_model)}.items():
+        a = torch.randn((m, kk), generator=gen, device="cuda", dtype=torch.float32).to(dt)
+        b = torch.randn((kk, n), generator=gen, device="cuda", dtype=torch.float32).to(dt)
+        c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * m * kk * n / (ms * 1e-3) / 1e12
+        out[name] = {"m": m, "k": kk, "n": n, "ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_backward(cfg, layer, x, steps: int, warmup: int):
@@ -383,6 +421,8 @@ def main():
         bw_bytes = layer.backward_workspace_bytes(cfg.T) + 4 * 3 * cfg.n_experts * cfg.d_model * cfg.d_ff
         if bw_bytes < 120e9:
             out["backward"] = measure_backward(cfg, layer, x, max(1, min(args.steps // 4, 50)), 2)
+    if args.library_gemm:
+        out["library_gemm"] = measure_library_gemm(cfg, max(3, min(args.steps, 20)))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_seconds)
     print(json.dumps(out), flush=True)
