@@ -559,6 +559,10 @@ int cu_count() {
 }
 
 
+// Rows per busy group up to which a grouped product counts as a batch of a
+// few tokens (gemm_bm, gemm_bn_caps).
+constexpr int64_t kFewRows = 32;
+
 // Row tile of a grouped GEMM: 256 rows when groups are long enough to fill
 // such tiles and there are enough of them to give every CU several (the
 // persistent grid has one 256-row block per CU), else 128 (less padding in
@@ -576,6 +580,11 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
   const int64_t busy = groups < rows ? groups : rows;
   const int64_t tiles64 = busy * (n % 128 == 0 ? n / 128 : n / 64);
   if (avg <= 128 && tiles64 >= 2 * (int64_t)cu_count()) return 64;
+  // A handful of rows per busy group (batches of a few tokens): every row
+  // tile is mostly padding, and its padding rows cost copies like weight
+  // rows do, so the shortest tile wins; gemm_bn_caps then narrows the weight
+  // tiles so that the few groups still spread over every CU.
+  if (rows <= kFewRows * busy) return 64;
   // 256-row tiles read each weight panel once per group: they pay for their
   // padding with many rows per group, or with a long K, where a 128-row
   // pair re-reads multi-MB panels that do not stay in L2 (d_in 7168: 3% at
@@ -583,6 +592,34 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
   const int64_t tiles256 = (rows / 256) * (n / 128);
   const bool long_k = d_in >= 4096;
   return ((avg >= 768 || long_k) && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
+}
+
+// Column-tile caps: none (0) unless gemm_bm took 64-row tiles for a handful
+// of rows per busy group where the widest tiles would not give every block
+// slot one; then gate/up and down each take the widest tile whose count over
+// the busy groups still spreads over every CU (measured against 128-row
+// tiles at 1-3 tokens of the DeepSeek-style layer: step 0.236 -> 0.215,
+// 0.393 -> 0.334, 0.466 -> 0.415 ms; 1 token of the Qwen3-like layer 0.079
+// -> 0.065 ms).
+GemmCaps gemm_bn_caps(int dtype, int64_t rows, int64_t groups, int n, int d_in, int d_out) {
+  GemmCaps c{0, 0};
+  if (dtype != 1 || groups <= 0 || gemm_bm(dtype, rows, groups, n, d_in) != 64) return c;
+  const int64_t busy = groups < rows ? groups : rows;
+  if (rows / groups <= 128 && busy * (n % 128 == 0 ? n / 128 : n / 64) >= 2 * (int64_t)cu_count()) return c;
+  // the widest tile whose count reaches `want`, else the narrowest: gate/up
+  // one tile per CU (measured at 2 tokens of the DeepSeek-style layer: 288
+  // tiles of 128 columns 186 us, 576 of 64 columns 191 us), down, whose K is
+  // the short d_ff, one and a half (1 token of the DeepSeek-style layer: 504
+  // tiles of 128 columns 43 us, 1008 of 64 columns 45 us; 2 tokens of the
+  // Qwen3-like layer: 256 tiles of 128 columns 16.5 us, 512 of 64 12.2 us)
+  auto cap = [&](int n_out, int widest, int64_t want) {
+    for (int bn = widest; bn > 64; bn /= 2)
+      if (n_out % bn == 0 && busy * (n_out / bn) >= want) return bn;
+    return 64;
+  };
+  c.gateup = cap(n, 128, cu_count());
+  c.down = cap(d_out, 256, 3 * (int64_t)cu_count() / 2);
+  return c;
 }
 
 // Row tile of a K-grouped (weight-gradient) GEMM: bf16 takes 256 x 256 tiles
@@ -661,12 +698,20 @@ hipError_t launch_gemm(const GemmLaunch& g, int bm, hipStream_t s) {
   }
   if (g.dtype == 1) {
     if (bm == 64) {
-      if (g.gateup)
-        return g.N % 128 == 0 ? launch_t<uint16_t, true, 64, 128, 128, 2>(g, s)
-                              : launch_t<uint16_t, true, 64, 64, 128, 2>(g, s);
-      if (g.N % 256 == 0) return launch_t<uint16_t, false, 64, 256, 128, 2>(g, s);
-      if (g.N % 128 == 0) return launch_t<uint16_t, false, 64, 128, 128, 2>(g, s);
-      return launch_t<uint16_t, false, 64, 64, 128, 2>(g, s);
+      // bn_cap set (a handful of rows per group): the narrowest tiles take a
+      // third stage buffer, so that each block keeps two weight stages in
+      // flight (measured at 1-2 tokens: DeepSeek-style gate/up 111 -> 104
+      // and 227 -> 186 us, Qwen3-like 1-token step 75 -> 65 us; with 64 x 128
+      // down tiles it was 3 us slower)
+      const int cap = g.bn_cap > 0 ? g.bn_cap : 256;
+      const bool deep = g.bn_cap > 0;
+      if (g.gateup) {
+        if (g.N % 128 == 0 && cap >= 128) return launch_t<uint16_t, true, 64, 128, 128, 2>(g, s);
+        return deep ? launch_t<uint16_t, true, 64, 64, 128, 3>(g, s) : launch_t<uint16_t, true, 64, 64, 128, 2>(g, s);
+      }
+      if (g.N % 256 == 0 && cap >= 256) return launch_t<uint16_t, false, 64, 256, 128, 2>(g, s);
+      if (g.N % 128 == 0 && cap >= 128) return launch_t<uint16_t, false, 64, 128, 128, 2>(g, s);
+      return deep ? launch_t<uint16_t, false, 64, 64, 128, 3>(g, s) : launch_t<uint16_t, false, 64, 64, 128, 2>(g, s);
     }
     if (g.gateup) {
       if (bm == 256 && g.N % 128 == 0) return launch_t<uint16_t, true, 256, 128, 128, 2>(g, s);

@@ -70,6 +70,7 @@ struct GemmLaunch {
   int dtype;               // 0 fp32, 1 bf16 (operands; accumulation fp32)
   bool gateup;             // true: out = silu(A B0^T) * (A B1^T) in dtype; false: out = A B0^T in fp32
   bool b_stream = false;   // weight rows read once (few rows per group): non-temporal DMA
+  int bn_cap = 0;          // forward products with 64-row tiles: widest column tile at most this (0: widest)
   const void* a;           // rows of K elements
   const int32_t* a_rows;   // null, or the source row of a for every grouped row (gather)
   int64_t a_row_count;     // rows of a (gather indices are clamped into range)
@@ -134,6 +135,12 @@ __host__ __device__ inline float* kg_out_row(const GemmLaunch& g, int grp, int m
 // columns of the gate/up product and its K = d_in; the tile list of a grouped
 // launch must be built with the same value.
 int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in);
+// Column-tile caps (GemmLaunch::bn_cap) of the forward gate/up and down
+// products with the row tile of gemm_bm; d_out = N of the down product.
+struct GemmCaps {
+  int gateup, down;
+};
+GemmCaps gemm_bn_caps(int dtype, int64_t rows, int64_t groups, int n, int d_in, int d_out);
 // Smallest row tile of a grouped launch: tile lists hold at most
 // rows / kMinTileRows + groups entries.
 constexpr int kMinTileRows = 64;

@@ -198,6 +198,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   if (merged && T * (int64_t)(k + 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
   const int n_groups = E + (merged ? 1 : 0);
   const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model);
+  const GemmCaps caps = gemm_bn_caps(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model, L->d_model);
   const int tpb = route_tokens_per_block(E, T, L->d_model);
   const int64_t nb_route = (T + tpb - 1) / tpb;
 
@@ -233,10 +234,12 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   gu.n_tiles = n_tiles;
   gu.max_m_tiles = lo.max_tiles;
   gu.b_stream = stream_weights(lo.gemm_rows, n_groups, bm);
+  gu.bn_cap = caps.gateup;
   MOE_TRY(launch_gemm_fwd(gu, bm, s));
   mark(tm, MOE_PHASE_DOWN, s);
   GemmLaunch dn = gu;
   dn.gateup = false;
+  dn.bn_cap = caps.down;
   dn.a = at<void>(ws, lo.h);
   dn.a_rows = nullptr;
   dn.b0 = L->w_down;
@@ -251,6 +254,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   // shared expert: rows T*k .. T*k+T-1 of the grouped output, or its own GEMMs
   const float* shared_out = merged ? at<float>(ws, lo.yperm) + (size_t)T * k * d : nullptr;
   const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared, L->d_model);
+  const GemmCaps caps_s = gemm_bn_caps(L->dtype, T, 1, L->d_ff_shared, L->d_model, L->d_model);
   mark(tm, MOE_PHASE_SHARED_GATEUP, s);
   if (L->d_ff_shared > 0 && !merged) {
     GemmLaunch sg{};
@@ -264,6 +268,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sg.K = d;
     sg.rows = T;
     sg.b_stream = stream_weights(T, 1, bm_s);
+    sg.bn_cap = caps_s.gateup;
     MOE_TRY(launch_gemm_fwd(sg, bm_s, s));
   }
   mark(tm, MOE_PHASE_SHARED_DOWN, s);
@@ -278,6 +283,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
     sd.K = L->d_ff_shared;
     sd.rows = T;
     sd.b_stream = stream_weights(T, 1, bm_s);
+    sd.bn_cap = caps_s.down;
     MOE_TRY(launch_gemm_fwd(sd, bm_s, s));
     shared_out = at<float>(ws, lo.ys);
   }
@@ -829,6 +835,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const int bm = gemm_bm(dtype, rows, n_groups, d_ff, d_in);
+  const GemmCaps caps = gemm_bn_caps(dtype, rows, n_groups, d_ff, d_in, d_in);
   const int64_t max_tiles = (rows + kMinTileRows - 1) / kMinTileRows + n_groups;
   int32_t* n_tiles = at<int32_t>(ws, 0);
   int2* tiles = at<int2>(ws, align_up(sizeof(int32_t)));
@@ -849,9 +856,11 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   gu.max_m_tiles = max_tiles;
   gu.n_groups = n_groups;
   gu.b_stream = stream_weights(rows, n_groups, bm);
+  gu.bn_cap = caps.gateup;
   MOE_TRY(launch_gemm_fwd(gu, bm, s));
   GemmLaunch dn = gu;
   dn.gateup = false;
+  dn.bn_cap = caps.down;
   dn.a = h;
   dn.b0 = w_down;
   dn.b1 = nullptr;

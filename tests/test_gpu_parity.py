@@ -35,6 +35,11 @@ CASES = [
     C("one_expert", T=130, d_model=64, n_experts=1, top_k=1, d_ff=64),
     C("k_equals_E", T=200, d_model=64, n_experts=4, top_k=4, d_ff=64, score="sigmoid"),
     C("single_token", T=1, d_model=64, n_experts=16, top_k=4, d_ff=128, shared=True),
+    # a few tokens over many experts: 64-row tiles with the column tiles
+    # narrowed until the busy groups cover every CU (gate/up 64 columns with
+    # three stage buffers, down 128 columns)
+    C("few_tokens_e64", T=3, d_model=2048, n_experts=64, top_k=8, d_ff=512, score="sigmoid", shared=True,
+      bias_range=0.1),
     # a few rows per expert over many experts: 64-row tiles, 64 x 128 gate/up
     # and 64 x 256 down weight tiles, the shared expert as one more group
     C("tiles64_e512_shared", T=700, d_model=256, n_experts=512, top_k=4, d_ff=128, score="sigmoid", shared=True,
