@@ -110,16 +110,19 @@ def shared_as_group(cfg) -> bool:
     return cfg.d_ff_s > 0 and cfg.d_ff_s == cfg.d_ff and cfg.T * cfg.d_ff_s <= 1 << 25
 
 
-def phase_bytes_and_flops(cfg):
-    """Algorithmic work per phase (activated experts only)."""
+def phase_bytes_and_flops(cfg, used=None):
+    """Algorithmic work per phase (activated experts only): `used` experts
+    received tokens (all of them when None), and only their weights count as
+    read."""
     T, d, E, k, f, fs = cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff, cfg.d_ff_s
+    Eu = E if used is None else used
     b = 2 if cfg.dtype == "bf16" else 4
     rows = T * k
     work = {
         # x, W_r in; ids, weights, ranks out
         "route": {"bytes": T * d * b + E * d * 4 + rows * 12, "flops": 2.0 * T * d * E},
-        "gateup": {"flops": 4.0 * rows * d * f, "bytes": rows * d * b + E * 2 * f * d * b + rows * f * b},
-        "down": {"flops": 2.0 * rows * f * d, "bytes": rows * f * b + E * d * f * b + rows * d * 4},
+        "gateup": {"flops": 4.0 * rows * d * f, "bytes": rows * d * b + Eu * 2 * f * d * b + rows * f * b},
+        "down": {"flops": 2.0 * rows * f * d, "bytes": rows * f * b + Eu * d * f * b + rows * d * 4},
         "shared_gateup": {"flops": 4.0 * T * d * fs, "bytes": (T * d * b + 2 * fs * d * b + T * fs * b) if fs else 0},
         "shared_down": {"flops": 2.0 * T * fs * d, "bytes": (T * fs * b + d * fs * b + T * d * 4) if fs else 0},
         # Y rows, weights and ids, shared rows in; y out
@@ -141,6 +144,8 @@ def gemm_row_tile(rows: int, groups: int, n: int, d_in: int, cu: int = 256) -> i
     busy = min(groups, rows)
     if avg <= 128 and busy * (n // 128 if n % 128 == 0 else n // 64) >= 2 * cu:
         return 64
+    if rows <= 32 * busy:  # a handful of rows per busy group
+        return 64
     long_k = d_in >= 4096
     return 256 if (avg >= 768 or long_k) and (rows // 256) * (n // 128) >= 4 * cu else 128
 
@@ -152,6 +157,22 @@ def gateup_kernel(cfg) -> str:
     if cfg.dtype == "bf16" and gemm_row_tile(rows, groups, cfg.d_ff, cfg.d_model) == 256 and cfg.d_ff % 128 == 0:
         return "k_gemm8<gate/up, grouped> (256 x 256 tiles, eight waves)"
     return f"k_gemm<{cfg.dtype}, gate/up, grouped>"
+
+
+def gateup_roofline(cfg, work, gateup_ms: float, traffic):
+    """Roofline of the routed gate/up launch: against the matrix cores when
+    its algorithmic flops per byte reach the ridge of the two peaks, else
+    (a few rows per expert) against HBM, the weights it must read."""
+    peak = PEAK_TFLOPS[cfg.dtype]
+    what = "routed experts + the shared expert as one more group" if shared_as_group(cfg) else "routed experts"
+    gw = work["gateup"]
+    if gw["flops"] / gw["bytes"] >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gu = gw["flops"] / (gateup_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": f"{gateup_kernel(cfg)} ({what})", "achieved": round(gu, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
+    gbs = gw["bytes"] / (gateup_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": f"{gateup_kernel(cfg)} ({what})", "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
 
 
 def measure_permute(cfg, layer, x, reps: int):
@@ -348,14 +369,14 @@ def main():
     for t in timings:
         t.close()
 
-    work = phase_bytes_and_flops(cfg)
+    # experts that received tokens: only their weights are read
+    counts = layer.route(x)["counts"].cpu().numpy()
+    used = int((counts > 0).sum())
+    work = phase_bytes_and_flops(cfg, used)
     peak = PEAK_TFLOPS[cfg.dtype]
-    gu = work["gateup"]["flops"] / (gateup_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile("gateup", args.workload)
-    what = "routed experts + the shared expert as one more group" if shared_as_group(cfg) else "routed experts"
-    roofline = {"bound": "mfma", "kernel": f"{gateup_kernel(cfg)} ({what})",
-                "achieved": round(gu, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(gu / peak, 4), "traffic": traffic}
+    # the committed counter summaries were taken at the workload's own size
+    traffic = traffic_from_profile("gateup", args.workload) if args.tokens in (0, CONFIGS[args.workload].T) else None
+    roofline = gateup_roofline(cfg, work, gateup_ms, traffic)
     def phase_detail(pms):
         detail = {}
         for name, w in work.items():
@@ -409,8 +430,6 @@ def main():
                                       "outside the timed events (L2 and the last-level cache evicted)")
     out["permute"] = measure_permute(cfg, layer, x, max(3, min(args.steps, 20)))
     # expert weights the step had to read: experts that received tokens (+ the shared one)
-    counts = layer.route(x)["counts"].cpu().numpy()
-    used = int((counts > 0).sum())
     wbytes = (2 if cfg.dtype == "bf16" else 4) * 3 * cfg.d_model * (used * cfg.d_ff + cfg.d_ff_s)
     gemm_ms = sum(phase_ms[n] for n in gemm_phases)
     out["expert_weights"] = {"experts_used": used, "bytes": wbytes,

@@ -105,3 +105,32 @@ def test_mfma_busy_and_clock(tmp_path, capsys):
     assert float(pf) == pytest.approx(2.5 * 1.5 / 2.4, abs=1e-2)
     assert float(gflop) == pytest.approx(2000.0, rel=1e-3)
     assert float(us) == pytest.approx(1000.0)
+
+
+def test_bench_work_and_roofline_choice():
+    """bench.py's algorithmic work: the DeepSeek-style layer's routed gate/up
+    (the shared expert runs on its own) is 4 T k d d_ff flops over the x rows,
+    every expert's gate and up weights and H; a batch that touches few experts
+    counts only their weights, and its gate/up launch, below the ridge of the
+    two peaks, is reported against HBM."""
+    import bench
+    from mixture_experts_ffn_02_amd.inputs import CONFIGS
+
+    cfg = CONFIGS["deepseek_fine"]
+    T, d, k, f, E = cfg.T, cfg.d_model, cfg.top_k, cfg.d_ff, cfg.n_experts
+    w = bench.phase_bytes_and_flops(cfg)
+    assert w["gateup"]["flops"] == 4.0 * T * k * d * f
+    assert w["gateup"]["bytes"] == T * k * d * 2 + E * 2 * f * d * 2 + T * k * f * 2 == 24696061952
+    r = bench.gateup_roofline(cfg, w, 28.0, None)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == pytest.approx(4.0 * T * k * d * f / 28e-3 / 1e12, rel=1e-3)
+
+    one = cfg.with_tokens(1)
+    w1 = bench.phase_bytes_and_flops(one, used=8)
+    assert "shared_gateup" not in w1  # the shared expert is one more group of the routed launches
+    weights = (8 * 2 * f * d + 2 * f * d) * 2
+    assert w1["gateup"]["bytes"] == (k + 1) * d * 2 + weights + (k + 1) * f * 2
+    r1 = bench.gateup_roofline(one, w1, 0.1, None)
+    assert r1["bound"] == "hbm" and r1["unit"] == "GB/s"
+    assert r1["achieved"] == pytest.approx(w1["gateup"]["bytes"] / 0.1e-3 / 1e9, rel=1e-3)
+    assert bench.gemm_row_tile((k + 1) * 1, E + 1, f, d) == 64
