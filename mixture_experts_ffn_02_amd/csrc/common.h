@@ -42,6 +42,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
