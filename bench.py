@@ -138,16 +138,27 @@ def phase_bytes_and_flops(cfg, used=None):
 
 
 def gemm_row_tile(rows: int, groups: int, n: int, d_in: int, cu: int = 256) -> int:
-    """The library's row tile for a bf16 grouped launch (host rule of
-    gemm.hip: 64 for few rows per group, 256 for many rows or a long K)."""
+    """The library's row tile for the forward products of a bf16 grouped
+    launch (host rules gemm_bm and gemm_bm_fwd of gemm.hip: 64 for few rows
+    per group, 256 for many rows or a long K, or where the eight-wave kernel
+    runs both products and the groups average more than 64 rows)."""
     avg = rows // max(groups, 1)
     busy = min(groups, rows)
-    if avg <= 128 and busy * (n // 128 if n % 128 == 0 else n // 64) >= 2 * cu:
-        return 64
-    if rows <= 32 * busy:  # a handful of rows per busy group
-        return 64
     long_k = d_in >= 4096
-    return 256 if (avg >= 768 or long_k) and (rows // 256) * (n // 128) >= 4 * cu else 128
+    if avg <= 128 and busy * (n // 128 if n % 128 == 0 else n // 64) >= 2 * cu:
+        bm = 64
+    elif rows <= 32 * busy:  # a handful of rows per busy group
+        bm = 64
+    else:
+        bm = 256 if (avg >= 768 or long_k) and (rows // 256) * (n // 128) >= 4 * cu else 128
+    if bm == 256 or rows <= 32 * busy:
+        return bm
+    fits8 = n % 128 == 0 and d_in % 256 == 0 and n >= 192 and d_in >= 192
+    if fits8 and avg > 64 and max(rows // 256, busy) * (n // 128) >= 2 * cu:
+        return 256
+    if bm == 64 and avg > 48 and d_in >= 2048 and groups >= 64:
+        return 128
+    return bm
 
 
 def gateup_kernel(cfg) -> str:

@@ -594,6 +594,31 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
   return ((avg >= 768 || long_k) && tiles256 >= 4 * (int64_t)cu_count()) ? 256 : 128;
 }
 
+// Row tile of the forward products: gemm_bm, except where the eight-wave
+// 256 x 256 kernel (gemm8.hip) runs both products (gate/up N % 128, down N =
+// d_in % 256): its 256-row tiles then win from 65 rows per group on average
+// as long as the row tiles give every CU two column strips (step times,
+// Qwen3-like layer at 2,048 / 4,096 / 8,192 tokens: 0.492 -> 0.416, 0.701 ->
+// 0.622, 1.18 -> 0.98 ms; DeepSeek-style at 2,048 / 3,072: 5.86 -> 5.73,
+// 7.11 -> 6.27 ms; iso-width at 512 / 1,024: 0.79 -> 0.67, 1.09 -> 0.84 ms;
+// the large layers' full batches already took these tiles), and with a K of
+// 2048 or more and many experts 128-row tiles beat 64-row ones above 48 rows
+// per group (DeepSeek-style at 1,536 tokens 5.61 -> 5.05 ms, Qwen3-like at
+// 1,024 0.396 -> 0.339 ms; the iso-width layer's 16 experts at 64 rows each
+// were 10% slower with them).
+int gemm_bm_fwd(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
+  const int bm = gemm_bm(dtype, rows, groups, n, d_in);
+  if (dtype != 1 || groups <= 0 || bm == 256) return bm;
+  const int64_t busy = groups < rows ? groups : rows;
+  if (rows <= kFewRows * busy) return bm;  // a few tokens
+  const int64_t avg = rows / groups;
+  const bool fits8 = n % 128 == 0 && d_in % 256 == 0 && n >= 3 * 64 && d_in >= 3 * 64;
+  const int64_t row_tiles = rows / 256 > busy ? rows / 256 : busy;
+  if (fits8 && avg > 64 && row_tiles * (n / 128) >= 2 * (int64_t)cu_count()) return 256;
+  if (bm == 64 && avg > 48 && d_in >= 2048 && groups >= 64) return 128;
+  return bm;
+}
+
 // Column-tile caps: none (0) unless gemm_bm took 64-row tiles for a handful
 // of rows per busy group where the widest tiles would not give every block
 // slot one; then gate/up and down each take the widest tile whose count over
@@ -603,7 +628,7 @@ int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in) {
 // -> 0.065 ms).
 GemmCaps gemm_bn_caps(int dtype, int64_t rows, int64_t groups, int n, int d_in, int d_out) {
   GemmCaps c{0, 0};
-  if (dtype != 1 || groups <= 0 || gemm_bm(dtype, rows, groups, n, d_in) != 64) return c;
+  if (dtype != 1 || groups <= 0 || gemm_bm_fwd(dtype, rows, groups, n, d_in) != 64) return c;
   const int64_t busy = groups < rows ? groups : rows;
   if (rows / groups <= 128 && busy * (n % 128 == 0 ? n / 128 : n / 64) >= 2 * (int64_t)cu_count()) return c;
   // the widest tile whose count reaches `want`, else the narrowest: gate/up

@@ -135,8 +135,11 @@ __host__ __device__ inline float* kg_out_row(const GemmLaunch& g, int grp, int m
 // columns of the gate/up product and its K = d_in; the tile list of a grouped
 // launch must be built with the same value.
 int gemm_bm(int dtype, int64_t rows, int64_t groups, int n, int d_in);
+// Row tile of the forward gate/up and down products (gemm_bm, or 256 where
+// the eight-wave kernel runs both and the groups are long enough).
+int gemm_bm_fwd(int dtype, int64_t rows, int64_t groups, int n, int d_in);
 // Column-tile caps (GemmLaunch::bn_cap) of the forward gate/up and down
-// products with the row tile of gemm_bm; d_out = N of the down product.
+// products with the row tile of gemm_bm_fwd; d_out = N of the down product.
 struct GemmCaps {
   int gateup, down;
 };

@@ -197,7 +197,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   const bool merged = shared_as_group(L, T);
   if (merged && T * (int64_t)(k + 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;  // row ids are int32
   const int n_groups = E + (merged ? 1 : 0);
-  const int bm = gemm_bm(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model);
+  const int bm = gemm_bm_fwd(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model);
   const GemmCaps caps = gemm_bn_caps(L->dtype, lo.gemm_rows, n_groups, L->d_ff, L->d_model, L->d_model);
   const int tpb = route_tokens_per_block(E, T, L->d_model);
   const int64_t nb_route = (T + tpb - 1) / tpb;
@@ -253,7 +253,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
 
   // shared expert: rows T*k .. T*k+T-1 of the grouped output, or its own GEMMs
   const float* shared_out = merged ? at<float>(ws, lo.yperm) + (size_t)T * k * d : nullptr;
-  const int bm_s = gemm_bm(L->dtype, T, 1, L->d_ff_shared, L->d_model);
+  const int bm_s = gemm_bm_fwd(L->dtype, T, 1, L->d_ff_shared, L->d_model);
   const GemmCaps caps_s = gemm_bn_caps(L->dtype, T, 1, L->d_ff_shared, L->d_model, L->d_model);
   mark(tm, MOE_PHASE_SHARED_GATEUP, s);
   if (L->d_ff_shared > 0 && !merged) {
@@ -834,7 +834,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  const int bm = gemm_bm(dtype, rows, n_groups, d_ff, d_in);
+  const int bm = gemm_bm_fwd(dtype, rows, n_groups, d_ff, d_in);
   const GemmCaps caps = gemm_bn_caps(dtype, rows, n_groups, d_ff, d_in, d_in);
   const int64_t max_tiles = (rows + kMinTileRows - 1) / kMinTileRows + n_groups;
   int32_t* n_tiles = at<int32_t>(ws, 0);

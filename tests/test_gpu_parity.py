@@ -77,7 +77,8 @@ CASES = [
 ]
 
 # Wide-expert layers whose grouped GEMMs run the tile shapes of the large
-# workload layers (256-row tiles), compared on every output element: many
+# workload layers (256-row tiles, and 128-row tiles over a long K), compared
+# on every output element: many
 # rows per expert (2048 on average, 2048 row tiles of 256), and a long K
 # (d_model 4096) with 256 rows per expert and the shared expert as a group; a Zipf-skewed router whose largest
 # group is most of the tokens beside experts with a few rows. The SwiGLU width
@@ -88,6 +89,11 @@ WIDE = [
     C("tiles256_long_k", T=2048, d_model=4096, n_experts=64, top_k=8, d_ff=2048, score="sigmoid", shared=True,
       bias_range=0.1),
     C("tiles256_zipf", T=8192, d_model=1024, n_experts=64, top_k=8, d_ff=768, zipf_s=1.1),
+    # the Qwen3-like layer's shape at 1,024 tokens (64 rows per expert: the
+    # forward rule's 128-row tiles for a long K) and at 2,048 (128 rows: the
+    # eight-wave kernel's 256-row tiles over short groups)
+    C("rows64_long_k", T=1024, d_model=2048, n_experts=128, top_k=8, d_ff=768, zipf_s=1.1),
+    C("rows128_tiles256", T=2048, d_model=2048, n_experts=128, top_k=8, d_ff=768, zipf_s=1.1),
 ]
 
 
