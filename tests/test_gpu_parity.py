@@ -40,6 +40,13 @@ CASES = [
     # three stage buffers, down 128 columns)
     C("few_tokens_e64", T=3, d_model=2048, n_experts=64, top_k=8, d_ff=512, score="sigmoid", shared=True,
       bias_range=0.1),
+    # a bf16 shared expert wider than the routed ones runs as its own dense
+    # launches: with 2 tokens on the 64-column three-buffer tiles, with 100 on
+    # 128-row tiles
+    C("wide_shared_2_tokens", T=2, d_model=256, n_experts=16, top_k=2, d_ff=128, score="sigmoid", shared=True,
+      d_ff_shared=384, bias_range=0.1),
+    C("wide_shared_100_tokens", T=100, d_model=256, n_experts=16, top_k=2, d_ff=128, score="sigmoid", shared=True,
+      d_ff_shared=384, bias_range=0.1),
     # a few rows per expert over many experts: 64-row tiles, 64 x 128 gate/up
     # and 64 x 256 down weight tiles, the shared expert as one more group
     C("tiles64_e512_shared", T=700, d_model=256, n_experts=512, top_k=4, d_ff=128, score="sigmoid", shared=True,
