@@ -135,7 +135,8 @@ struct Tile8 {
 };
 
 // STREAM: weight copies non-temporal (each weight tile read about once).
-template <bool GATEUP, bool GROUPED, bool STREAM>
+// BYGROUP: raster groups inside each group's row tiles (see tile_at).
+template <bool GATEUP, bool GROUPED, bool STREAM, bool BYGROUP = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void k_gemm8(GemmLaunch g) {
   __shared__ __align__(16) unsigned char lds[kNH * kHalf];
@@ -173,14 +174,37 @@ void k_gemm8(GemmLaunch g) {
   // The block's tiles, in raster order: 8 contiguous ranges of the order,
   // one per XCD, each walked in groups of group_m row tiles x all column
   // tiles; a tile of the device-side list naming no group, or with no rows,
-  // is skipped.
+  // is skipped. BYGROUP cuts the raster groups inside each group's (expert's)
+  // row tiles instead of across the whole list, so that no raster group
+  // mixes two experts' weight panels: group e's row tiles are list entries
+  // T_e .. T_e + r_e - 1 and its tiles raster positions T_e n_tiles_n ..
+  // (T_e + r_e) n_tiles_n - 1, walked in ceil(r_e / group_m) chunks of
+  // equal size.
   auto tile_at = [&](int64_t L, Tile8& t) -> bool {
-    const int64_t gsz = (int64_t)group_m * n_tiles_n;
-    const int64_t first_m = (L / gsz) * group_m;
-    const int64_t gm = (m_tiles - first_m) < group_m ? (m_tiles - first_m) : group_m;
-    const int64_t within = L % gsz;
-    const int64_t tile_m = first_m + within % gm;
-    const int tile_n = (int)(within / gm);
+    int64_t tile_m;
+    int tile_n;
+    if constexpr (GROUPED && BYGROUP) {
+      const int64_t m0 = L / n_tiles_n;
+      const int2 h = g.tiles[m0];
+      if (h.x < 0 || h.x >= g.n_groups || h.y < 0) return false;
+      const int64_t te = m0 - h.y;
+      const int64_t re = ((int64_t)g.offsets[h.x + 1] - g.offsets[h.x] + kBM - 1) / kBM;
+      const int64_t nc = (re + group_m - 1) / group_m;
+      const int64_t cs = (re + nc - 1) / nc;
+      const int64_t within = L - te * n_tiles_n;
+      const int64_t c = within / (cs * n_tiles_n);
+      const int64_t gm = (re - c * cs) < cs ? (re - c * cs) : cs;
+      const int64_t w2 = within - c * cs * n_tiles_n;
+      tile_m = te + c * cs + w2 % gm;
+      tile_n = (int)(w2 / gm);
+    } else {
+      const int64_t gsz = (int64_t)group_m * n_tiles_n;
+      const int64_t first_m = (L / gsz) * group_m;
+      const int64_t gm = (m_tiles - first_m) < group_m ? (m_tiles - first_m) : group_m;
+      const int64_t within = L % gsz;
+      tile_m = first_m + within % gm;
+      tile_n = (int)(within / gm);
+    }
     t.n0 = GATEUP ? tile_n * 128 : tile_n * 256;
     if constexpr (GROUPED) {
       const int2 tl = g.tiles[tile_m];
@@ -515,7 +539,8 @@ hipError_t launch_gemm8(const GemmLaunch& g, hipStream_t s) {
   auto go = [&](auto kern) __attribute__((always_inline)) { hipLaunchKernelGGL(kern, grid, block, 0, s, g); };
   if (g.gateup) {
     if (g.offsets) {
-      if (g.b_stream) go(k_gemm8<true, true, true>); else go(k_gemm8<true, true, false>);
+      if (g.raster_by_group && !g.b_stream) go(k_gemm8<true, true, false, true>);
+      else if (g.b_stream) go(k_gemm8<true, true, true>); else go(k_gemm8<true, true, false>);
     } else {
       if (g.b_stream) go(k_gemm8<true, false, true>); else go(k_gemm8<true, false, false>);
     }

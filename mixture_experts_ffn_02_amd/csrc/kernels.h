@@ -71,6 +71,7 @@ struct GemmLaunch {
   bool gateup;             // true: out = silu(A B0^T) * (A B1^T) in dtype; false: out = A B0^T in fp32
   bool b_stream = false;   // weight rows read once (few rows per group): non-temporal DMA
   int bn_cap = 0;          // forward products with 64-row tiles: widest column tile at most this (0: widest)
+  bool raster_by_group = false;  // grouped eight-wave gate/up: raster groups stay inside each group's row tiles
   const void* a;           // rows of K elements
   const int32_t* a_rows;   // null, or the source row of a for every grouped row (gather)
   int64_t a_row_count;     // rows of a (gather indices are clamped into range)
