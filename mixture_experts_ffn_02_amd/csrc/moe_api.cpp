@@ -62,14 +62,17 @@ bool stream_weights(int64_t rows, int64_t groups, int bm) {
 
 // The routed gate/up launch of the eight-wave kernel walks its raster groups
 // inside each expert's row tiles when there are many experts averaging four
-// or more 256-row tiles: a raster group of 8 row tiles across the list then
-// mixes two experts' weight panels in most of its rounds. Measured on the
-// DeepSeek-style layer (8.5 row tiles per expert) 27.3 -> 26.8 ms; the
-// Qwen3-like layer (4 on average, Zipf-skewed) within noise; its down launch
-// 2% slower that way, so down keeps the plain order; the iso-width layer's
-// 16 experts of 32 row tiles keep it too (0.6% slower).
-bool raster_by_group(int64_t rows, int64_t groups) {
-  return groups >= 64 && rows >= groups * 4 * (int64_t)256;
+// or more 256-row tiles, or two or more with a K of at least 4096 (multi-MB
+// weight panels): a raster group of 8 row tiles across the list then mixes
+// several experts' weight panels in most of its rounds. Measured on the
+// DeepSeek-style layer (8.5 row tiles per expert) 28.2 -> 27.7 ms, and at
+// 16,384 tokens (2.2 per expert) 9.60 -> 9.32 ms; the Qwen3-like layer (K
+// 2048) within noise at 4 row tiles per expert and 1.3% slower at 3; down
+// launches 2% slower that way, so down keeps the plain order; the iso-width
+// layer's 16 experts of 32 row tiles keep it too (0.6% slower).
+bool raster_by_group(int64_t rows, int64_t groups, int d_in) {
+  if (groups < 64) return false;
+  return rows >= groups * 4 * (int64_t)256 || (d_in >= 4096 && rows >= groups * 2 * (int64_t)256);
 }
 
 // The backward adds the router's input gradient dl W_router inside the final
@@ -247,7 +250,7 @@ moe_status forward_impl(const moe_layer* L, const void* x, int64_t T, const moe_
   gu.max_m_tiles = lo.max_tiles;
   gu.b_stream = stream_weights(lo.gemm_rows, n_groups, bm);
   gu.bn_cap = caps.gateup;
-  gu.raster_by_group = raster_by_group(lo.gemm_rows, n_groups);
+  gu.raster_by_group = raster_by_group(lo.gemm_rows, n_groups, L->d_model);
   MOE_TRY(launch_gemm_fwd(gu, bm, s));
   mark(tm, MOE_PHASE_DOWN, s);
   GemmLaunch dn = gu;
@@ -871,7 +874,7 @@ moe_status moe_grouped_swiglu(int32_t dtype, int32_t n_groups, int32_t d_in, int
   gu.n_groups = n_groups;
   gu.b_stream = stream_weights(rows, n_groups, bm);
   gu.bn_cap = caps.gateup;
-  gu.raster_by_group = raster_by_group(rows, n_groups);
+  gu.raster_by_group = raster_by_group(rows, n_groups, d_in);
   MOE_TRY(launch_gemm_fwd(gu, bm, s));
   GemmLaunch dn = gu;
   dn.gateup = false;
