@@ -101,9 +101,11 @@ WIDE = [
     # eight-wave kernel's 256-row tiles over short groups)
     C("rows64_long_k", T=1024, d_model=2048, n_experts=128, top_k=8, d_ff=768, zipf_s=1.1),
     C("rows128_tiles256", T=2048, d_model=2048, n_experts=128, top_k=8, d_ff=768, zipf_s=1.1),
-    # two 256-row tiles per expert on average over a K of 4096: the gate/up
-    # launch walks its raster groups inside each expert's row tiles
-    C("two_tiles_long_k", T=4096, d_model=4096, n_experts=64, top_k=8, d_ff=768, score="sigmoid", bias_range=0.1),
+    # two 256-row tiles per expert on average over a K of 4096, and the
+    # shared expert as a 65th group of 16 row tiles: the gate/up launch walks
+    # its raster groups inside each group's row tiles
+    C("two_tiles_long_k", T=4096, d_model=4096, n_experts=64, top_k=8, d_ff=768, score="sigmoid", shared=True,
+      bias_range=0.1),
 ]
 
 
