@@ -134,3 +134,33 @@ def test_bench_work_and_roofline_choice():
     assert r1["bound"] == "hbm" and r1["unit"] == "GB/s"
     assert r1["achieved"] == pytest.approx(w1["gateup"]["bytes"] / 0.1e-3 / 1e9, rel=1e-3)
     assert bench.gemm_row_tile((k + 1) * 1, E + 1, f, d) == 64
+
+
+def test_bench_row_tile_follows_the_library():
+    """bench.py names the gate/up kernel and its tile from a Python copy of the
+    library's forward row-tile rule; the copy gives the library's own answer
+    (its exported host function, with the 256 CUs it assumes when no device
+    is visible) on layers from one row to the DeepSeek-style batch, one group
+    to 257, and the widths and K of the workload layers."""
+    import ctypes
+
+    import bench
+    from mixture_experts_ffn_02_amd import _native as N
+
+    lib = N.load()
+    cu = getattr(lib, "_ZN3moe8cu_countEv")
+    cu.restype = ctypes.c_int
+    if cu() != 256:
+        pytest.skip("a device with another CU count is visible")
+    rule = getattr(lib, "_ZN3moe11gemm_bm_fwdEillii")
+    rule.restype = ctypes.c_int
+    rule.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int]
+    n_checked = 0
+    for rows in (1, 3, 24, 100, 1000, 4096, 16384, 36864, 131072, 147456, 524288):
+        for groups in (1, 16, 64, 65, 128, 129, 256, 257):
+            for n in (64, 192, 256, 768, 1024, 2048, 4352):
+                for d_in in (64, 512, 2048, 4096, 5120, 7168):
+                    assert bench.gemm_row_tile(rows, groups, n, d_in) == rule(1, rows, groups, n, d_in), \
+                        (rows, groups, n, d_in)
+                    n_checked += 1
+    assert n_checked == 11 * 8 * 7 * 6
