@@ -239,7 +239,8 @@ void k_gemm8(GemmLaunch g) {
   // Per tile, for the copies (block-uniform bases and size; down builds
   // buffer resources from them): the row of abase that each of this lane's
   // A runs reads (run 8 i + wave covers tile rows 64 i + 8 wave .. +7; rows
-  // past the tile's end read a valid row whose results are never stored)
+  // past the tile's end read a valid row, or nothing, and their results are
+  // never stored)
   // and the weight bases (gate/up: runs with i >= 2 are up rows). Gathered
   // rows index all of A, contiguous ones the tile's own rows.
   struct Src {
@@ -261,7 +262,11 @@ void k_gemm8(GemmLaunch g) {
 #pragma unroll
     for (int i = 0; i < kRuns; ++i) {
       int r = 8 * (kSlots * i + wave) + lrow;
-      r = r < t.rows ? r : t.rows - 1;
+      // rows past the tile's end copy its last row, except in down products
+      // of contiguous rows: there they stay past the end of the copy's buffer
+      // range, so the hardware drops them (nothing fetched; the copy is still
+      // issued and counted by the stage waits)
+      if (GATEUP || g.a_rows) r = r < t.rows ? r : t.rows - 1;
       int64_t src = r;
       if (g.a_rows) {
         src = g.a_rows[t.row0 + r];
